@@ -1,0 +1,228 @@
+"""Python binding of the gfx950 attention library (libattn_fa2.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/attn_fa2.h.  PyTorch supplies
+device memory (outputs are allocated with torch.empty when not given) and the
+current stream.  There is no fallback: if the library is missing or a call
+fails, an exception is raised.
+
+Functions (same names as the C entry points):
+    attn_fwd(q, k, v, ...)                      -> (out, lse)
+    attn_build_block_mask(mask, B, Sq, Skv, ...) -> BlockMask
+    attn_paged_decode_workspace_size(...)       -> int (bytes)
+    attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, ...) -> (out, lse)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_fa2.so")
+
+F32, BF16 = 0, 1
+MASK_KINDS = {"none": 0, "causal": 1, "sliding": 2, "prefix_lm": 3, "document": 4}
+SCORE_KINDS = {"none": 0, "alibi": 1, "rel_pos": 2}
+EXPORTED = ("attn_fwd", "attn_build_block_mask", "attn_paged_decode_workspace_size",
+            "attn_paged_decode", "attn_last_error")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with code {code}: {msg}")
+        self.code = code
+
+
+class MaskParams(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("prefix_len", ctypes.c_int32),
+                ("doc_ids", ctypes.c_void_p)]
+
+
+class ScoreParams(ctypes.Structure):
+    _fields_ = [("alibi_slopes", ctypes.c_void_p), ("rel_scale", ctypes.c_float)]
+
+
+class BlockMaskC(ctypes.Structure):
+    _fields_ = [("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
+                ("kv_full", ctypes.c_void_p), ("q_block", ctypes.c_int32),
+                ("kv_block", ctypes.c_int32), ("n_q_blocks", ctypes.c_int32),
+                ("n_kv_blocks", ctypes.c_int32), ("batch", ctypes.c_int32)]
+
+
+@dataclass
+class BlockMask:
+    kv_num_blocks: torch.Tensor    # int32 [B, 1, nQB]
+    kv_indices: torch.Tensor       # int32 [B, 1, nQB, nKVB]
+    kv_full: Optional[torch.Tensor]  # uint8 [B, 1, nQB, nKVB]
+    q_block: int
+    kv_block: int
+
+    def to_c(self) -> BlockMaskC:
+        b, _, nqb, nkb = self.kv_indices.shape
+        return BlockMaskC(self.kv_num_blocks.data_ptr(), self.kv_indices.data_ptr(),
+                          self.kv_full.data_ptr() if self.kv_full is not None else None,
+                          self.q_block, self.kv_block, nqb, nkb, b)
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn_fa2.so (built by attention_fa2_fwd_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m attention_fa2_fwd_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                             i32, ctypes.POINTER(MaskParams), i32, ctypes.POINTER(ScoreParams),
+                             ctypes.POINTER(BlockMaskC), vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_build_block_mask.argtypes = [i32, ctypes.POINTER(MaskParams), i32, i32, i32, i32,
+                                          i32, vp, vp, vp, vp]
+    lib.attn_build_block_mask.restype = i32
+    lib.attn_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_paged_decode_workspace_size.restype = ctypes.c_size_t
+    lib.attn_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                      i32, i32, f32, i32, ctypes.POINTER(ScoreParams), vp,
+                                      ctypes.c_size_t, vp]
+    lib.attn_paged_decode.restype = i32
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        msg = load_library().attn_last_error().decode(errors="replace")
+        raise AttnError(fn, rc, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_device(*tensors):
+    for t in tensors:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device (GPU) tensors")
+
+
+def _mask_params(mask: str, window: int, prefix_len: int, doc_ids: Optional[torch.Tensor]):
+    if mask not in MASK_KINDS:
+        raise ValueError(f"unknown mask kind {mask!r}")
+    if doc_ids is not None and doc_ids.dtype != torch.int32:
+        raise ValueError("doc_ids must be int32")
+    return MASK_KINDS[mask], MaskParams(int(window), int(prefix_len), _ptr(doc_ids))
+
+
+def _score_params(score: str, alibi_slopes: Optional[torch.Tensor], rel_scale: float):
+    if score not in SCORE_KINDS:
+        raise ValueError(f"unknown score kind {score!r}")
+    if alibi_slopes is not None and alibi_slopes.dtype != torch.float32:
+        raise ValueError("alibi_slopes must be float32")
+    return SCORE_KINDS[score], ScoreParams(_ptr(alibi_slopes), float(rel_scale))
+
+
+def attn_fwd(q, k, v, *, scale: Optional[float] = None, mask: str = "none", window: int = 0,
+             prefix_len: int = 0, doc_ids=None, score: str = "none", alibi_slopes=None,
+             rel_scale: float = 1.0, block_mask: Optional[BlockMask] = None, out=None, lse=None,
+             out_dtype=None):
+    """Fused attention forward.  q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] (bf16 or fp32).
+    Returns (out [B,Hq,Sq,D], lse [B,Hq,Sq] float32).  out_dtype defaults to
+    the input dtype; torch.float32 gives bf16 inputs an fp32 output."""
+    lib = load_library()
+    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype bf16 or float32")
+    b, hq, sq, d = q.shape
+    hkv, skv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be bf16 or float32")
+    if lse is None:
+        lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    _need_device(q, k, v, out, lse, doc_ids, alibi_slopes)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mk, mp = _mask_params(mask, window, prefix_len, doc_ids)
+    sk, sp = _score_params(score, alibi_slopes, rel_scale)
+    bmc = block_mask.to_c() if block_mask is not None else None
+    rc = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      BF16 if q.dtype == torch.bfloat16 else F32,
+                      BF16 if out.dtype == torch.bfloat16 else F32, b, hq, hkv, sq, skv, d,
+                      float(scale), mk, ctypes.byref(mp), sk, ctypes.byref(sp),
+                      ctypes.byref(bmc) if bmc is not None else None, _stream(q.device))
+    _check("attn_fwd", rc)
+    return out, lse
+
+
+def attn_build_block_mask(mask: str, B: int, Sq: int, Skv: int, *, q_block: int = 128,
+                          kv_block: int = 128, window: int = 0, prefix_len: int = 0,
+                          doc_ids=None, device="cuda", with_full: bool = True) -> BlockMask:
+    """Build the BlockMask of a mask kind on the GPU."""
+    lib = load_library()
+    device = torch.device(device)
+    nqb = -(-Sq // q_block)
+    nkb = -(-Skv // kv_block)
+    num = torch.empty((B, 1, nqb), dtype=torch.int32, device=device)
+    idx = torch.empty((B, 1, nqb, nkb), dtype=torch.int32, device=device)
+    full = torch.empty((B, 1, nqb, nkb), dtype=torch.uint8, device=device) if with_full else None
+    _need_device(num, idx, full, doc_ids)
+    mk, mp = _mask_params(mask, window, prefix_len, doc_ids)
+    rc = lib.attn_build_block_mask(mk, ctypes.byref(mp), B, Sq, Skv, q_block, kv_block,
+                                   num.data_ptr(), idx.data_ptr(), _ptr(full), _stream(device))
+    _check("attn_build_block_mask", rc)
+    return BlockMask(num, idx, full, q_block, kv_block)
+
+
+def attn_paged_decode_workspace_size(num_seqs: int, Hq: int, D: int, max_pages_per_seq: int,
+                                     page_size: int = 16) -> int:
+    return int(load_library().attn_paged_decode_workspace_size(num_seqs, Hq, D,
+                                                                max_pages_per_seq, page_size))
+
+
+def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optional[float] = None,
+                      score: str = "none", alibi_slopes=None, rel_scale: float = 1.0,
+                      workspace=None, out=None, lse=None):
+    """Paged split-KV decode.  q [N,Hq,D] bf16; caches [pages,Hkv,page,D] bf16;
+    page_table int32 [N,max_pages]; seq_lens int32 [N].  Returns (out, lse)."""
+    lib = load_library()
+    n, hq, d = q.shape
+    pages, hkv, page_size, _ = k_cache.shape
+    max_pages = page_table.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+    need = attn_paged_decode_workspace_size(n, hq, d, max_pages, page_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("page_table and seq_lens must be int32")
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise ValueError("paged decode takes bf16 q and caches")
+    _need_device(q, k_cache, v_cache, page_table, seq_lens, out, lse, workspace, alibi_slopes)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sk, sp = _score_params(score, alibi_slopes, rel_scale)
+    rc = lib.attn_paged_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                               page_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), BF16, n, hq, hkv, d, page_size, max_pages, pages,
+                               float(scale), sk, ctypes.byref(sp), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check("attn_paged_decode", rc)
+    return out, lse

@@ -1,0 +1,231 @@
+// C ABI of the attention library: argument validation, kernel selection and
+// launch on the caller's stream.  Every check runs on the host before any
+// launch; the library allocates nothing and never synchronises.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool valid_mask_kind(int mk) { return mk >= ATTN_MASK_NONE && mk <= ATTN_MASK_DOCUMENT; }
+bool valid_score_kind(int sk) { return sk >= ATTN_SCORE_NONE && sk <= ATTN_SCORE_REL_POS; }
+
+// Shared checks of mask parameters; fills the kernel-side copy.
+int check_mask(int mk, const attn_mask_params_t *mp, int Sq, int Skv, attn::MaskArgs *out) {
+  if (!valid_mask_kind(mk)) return fail(ATTN_ERR_INVALID, "unknown mask kind %d", mk);
+  out->kind = mk;
+  out->window = 0;
+  out->prefix_len = 0;
+  out->doc_ids = nullptr;
+  out->doc_stride = Skv;
+  if (mk == ATTN_MASK_SLIDING) {
+    if (!mp) return fail(ATTN_ERR_INVALID, "SLIDING mask needs mask params");
+    if (mp->window < 1) return fail(ATTN_ERR_INVALID, "window must be >= 1 (got %d)", mp->window);
+    out->window = mp->window;
+  } else if (mk == ATTN_MASK_PREFIX_LM) {
+    if (!mp) return fail(ATTN_ERR_INVALID, "PREFIX_LM mask needs mask params");
+    if (mp->prefix_len < 0) return fail(ATTN_ERR_INVALID, "prefix_len must be >= 0");
+    out->prefix_len = mp->prefix_len;
+  } else if (mk == ATTN_MASK_DOCUMENT) {
+    if (!mp || !mp->doc_ids) return fail(ATTN_ERR_INVALID, "DOCUMENT mask needs doc_ids");
+    if (Sq != Skv) return fail(ATTN_ERR_UNSUPPORTED, "DOCUMENT mask needs Sq == Skv");
+    out->doc_ids = mp->doc_ids;
+  }
+  return ATTN_OK;
+}
+
+int check_score(int sk, const attn_score_params_t *sp, attn::ScoreArgs *out) {
+  if (!valid_score_kind(sk)) return fail(ATTN_ERR_INVALID, "unknown score kind %d", sk);
+  out->kind = sk;
+  out->slopes = sp ? sp->alibi_slopes : nullptr;
+  out->rel_scale = sp ? sp->rel_scale : 1.0f;
+  if (sk == ATTN_SCORE_REL_POS && !sp) return fail(ATTN_ERR_INVALID, "REL_POS needs score params");
+  return ATTN_OK;
+}
+
+int launch_result(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_last_error(void) { return g_err; }
+
+int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+             attn_dtype_t dt, attn_dtype_t out_dt, int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+             attn_mask_kind_t mk, const attn_mask_params_t *mp, attn_score_kind_t sk,
+             const attn_score_params_t *sp, const attn_block_mask_t *bm, void *stream) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || D <= 0)
+    return fail(ATTN_ERR_INVALID, "negative size (B=%d Hq=%d Hkv=%d Sq=%d Skv=%d D=%d)", B, Hq,
+                Hkv, Sq, Skv, D);
+  if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0))
+    return fail(ATTN_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  if (dt != ATTN_BF16 && dt != ATTN_F32) return fail(ATTN_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (out_dt != ATTN_BF16 && out_dt != ATTN_F32)
+    return fail(ATTN_ERR_INVALID, "unknown output dtype %d", (int)out_dt);
+  if (dt == ATTN_F32 && out_dt != ATTN_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "fp32 inputs need an fp32 output");
+  if (dt == ATTN_BF16 && D != 64 && D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "bf16 path supports D in {64, 128} (got %d)", D);
+  if (dt == ATTN_F32 && D != 16 && D != 32 && D != 64 && D != 128 && D != 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "fp32 path supports D in {16, 32, 64, 128, 256} (got %d)", D);
+  attn::FwdParams p{};
+  int rc = check_mask(mk, mp, Sq, Skv, &p.mask);
+  if (rc) return rc;
+  rc = check_score(sk, sp, &p.score);
+  if (rc) return rc;
+  if (!(scale == scale)) return fail(ATTN_ERR_INVALID, "scale is NaN");
+  if (bm) {
+    if (!bm->kv_num_blocks || !bm->kv_indices)
+      return fail(ATTN_ERR_INVALID, "block mask needs kv_num_blocks and kv_indices");
+    if (bm->q_block != 128 || bm->kv_block != 128)
+      return fail(ATTN_ERR_UNSUPPORTED, "block mask must use 128 x 128 blocks (got %d x %d)",
+                  bm->q_block, bm->kv_block);
+    if (bm->n_q_blocks != (Sq + 127) / 128 || bm->n_kv_blocks != (Skv + 127) / 128)
+      return fail(ATTN_ERR_INVALID, "block mask shape %d x %d does not match Sq=%d Skv=%d",
+                  bm->n_q_blocks, bm->n_kv_blocks, Sq, Skv);
+    if (bm->batch != 1 && bm->batch != B)
+      return fail(ATTN_ERR_INVALID, "block mask batch %d must be 1 or B=%d", bm->batch, B);
+    p.bm_num = bm->kv_num_blocks;
+    p.bm_idx = bm->kv_indices;
+    p.bm_full = bm->kv_full;
+    p.bm_nqb = bm->n_q_blocks;
+    p.bm_nkb = bm->n_kv_blocks;
+    p.bm_batch = bm->batch;
+    p.bm_kv_block = bm->kv_block;
+  }
+  if (B == 0 || Hq == 0 || Sq == 0) {
+    g_err[0] = '\0';
+    return ATTN_OK;
+  }
+  if (!q || !out || !lse || (Skv > 0 && (!k || !v)))
+    return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  const double rows = (double)B * Hq * ((Sq + 127) / 128);
+  if (rows > 2147483647.0) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Skv = Skv;
+  p.D = D;
+  p.out_f32 = (out_dt == ATTN_F32);
+  p.scale = scale;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == ATTN_BF16) return launch_result(attn::launch_fwd_bf16(p, s), "attn_fwd (bf16)");
+  return launch_result(attn::launch_fwd_f32(p, s), "attn_fwd (fp32)");
+}
+
+int attn_build_block_mask(attn_mask_kind_t mk, const attn_mask_params_t *mp, int B, int Sq,
+                          int Skv, int q_block, int kv_block, int32_t *kv_num_blocks,
+                          int32_t *kv_indices, uint8_t *kv_full, void *stream) {
+  if (B < 0 || Sq < 0 || Skv < 0) return fail(ATTN_ERR_INVALID, "negative size");
+  if (q_block < 16 || q_block > 1024 || q_block % 16 || kv_block < 16 || kv_block > 1024 ||
+      kv_block % 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "block sizes must be multiples of 16 in [16, 1024]");
+  attn::BlockMaskParams p{};
+  int rc = check_mask(mk, mp, Sq, Skv, &p.mask);
+  if (rc) return rc;
+  if (B == 0 || Sq == 0) {
+    g_err[0] = '\0';
+    return ATTN_OK;
+  }
+  if (!kv_num_blocks || (Skv > 0 && !kv_indices)) return fail(ATTN_ERR_INVALID, "null output pointer");
+  p.B = B;
+  p.Sq = Sq;
+  p.Skv = Skv;
+  p.q_block = q_block;
+  p.kv_block = kv_block;
+  p.nqb = (Sq + q_block - 1) / q_block;
+  p.nkb = (Skv + kv_block - 1) / kv_block;
+  p.num = kv_num_blocks;
+  p.idx = kv_indices;
+  p.full = kv_full;
+  return launch_result(attn::launch_block_mask(p, (hipStream_t)stream), "attn_build_block_mask");
+}
+
+size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int D, int max_pages_per_seq,
+                                        int page_size) {
+  (void)page_size;
+  if (num_seqs <= 0 || Hq <= 0 || D <= 0 || max_pages_per_seq <= 0) return 0;
+  int split_pages = 0, max_splits = 0;
+  attn::decode_split_geometry(max_pages_per_seq, &split_pages, &max_splits);
+  const size_t rows = (size_t)num_seqs * Hq * max_splits;
+  const size_t o_bytes = (rows * D * sizeof(float) + 255) / 256 * 256;
+  return o_bytes + rows * sizeof(float);
+}
+
+int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *page_table, const int32_t *seq_lens, void *out, float *lse,
+                      attn_dtype_t dt, int N, int Hq, int Hkv, int D, int page_size,
+                      int max_pages_per_seq, int num_pages, float scale, attn_score_kind_t sk,
+                      const attn_score_params_t *sp, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  if (N < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
+      num_pages < 0)
+    return fail(ATTN_ERR_INVALID, "bad size (N=%d Hq=%d Hkv=%d D=%d page=%d max_pages=%d pool=%d)",
+                N, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages);
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports bf16 only");
+  if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports D == 128 (got %d)", D);
+  if (page_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports page_size == 16");
+  if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports Hq/Hkv <= 16");
+  attn::DecodeParams p{};
+  int rc = check_score(sk, sp, &p.score);
+  if (rc) return rc;
+  if (N == 0) {
+    g_err[0] = '\0';
+    return ATTN_OK;
+  }
+  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out || !lse)
+    return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  const size_t need = attn_paged_decode_workspace_size(N, Hq, D, max_pages_per_seq, page_size);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (((uintptr_t)workspace) % 256 != 0) return fail(ATTN_ERR_INVALID, "workspace must be 256-byte aligned");
+  int split_pages = 0, max_splits = 0;
+  attn::decode_split_geometry(max_pages_per_seq, &split_pages, &max_splits);
+  const size_t rows = (size_t)N * Hq * max_splits;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.page_table = page_table;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.lse = lse;
+  p.N = N;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.page_size = page_size;
+  p.max_pages = max_pages_per_seq;
+  p.num_pages = num_pages;
+  p.scale = scale;
+  p.ws_o = (float *)workspace;
+  p.ws_lse = (float *)((char *)workspace + (rows * D * sizeof(float) + 255) / 256 * 256);
+  p.max_splits = max_splits;
+  p.split_pages = split_pages;
+  return launch_result(attn::launch_paged_decode(p, (hipStream_t)stream), "attn_paged_decode");
+}
+
+}  // extern "C"

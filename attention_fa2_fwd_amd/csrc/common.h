@@ -1,0 +1,84 @@
+// Device-side definitions shared by the attention kernels (gfx950 / CDNA4).
+//
+// The mask predicates and score modifiers follow the FlexAttention write-up
+// "新PyTorch API：几行代码实现不同注意力变体，兼具FlashAttention性能和PyTorch
+// 灵活性": §FlexAttention (score_mod applied to every score before softmax,
+// indexed by (b, h, q_idx, kv_idx)), §相对位置编码 (bias from the query-key
+// distance computed in-kernel), §Causal Mask, §Sliding Window + Causal, and
+// the PrefixLM / document-mask / ALiBi entries of its variant list.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/attn_fa2.h"
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Kernel-side copy of the mask parameters (plain values, passed by value).
+struct MaskArgs {
+  int kind;
+  int window;
+  int prefix_len;
+  const int32_t *doc_ids;  // [B, S]
+  int doc_stride;          // S
+};
+
+// Kernel-side score-modifier parameters. For ALIBI the per-head slope is read
+// from `slopes` or, when null, computed as 2^(-8 (h+1) / Hq).
+struct ScoreArgs {
+  int kind;
+  const float *slopes;
+  float rel_scale;
+};
+
+// visible(b, i, j) of the mask kind.  doc_i is doc_ids[b, i] (read once per
+// query row by the caller); the key's id is read here only for DOCUMENT.
+__device__ __forceinline__ bool mask_visible(const MaskArgs &m, int i, int j, int doc_i,
+                                             const int32_t *doc_row) {
+  switch (m.kind) {
+    case ATTN_MASK_NONE: return true;
+    case ATTN_MASK_CAUSAL: return j <= i;
+    case ATTN_MASK_SLIDING: return (j <= i) && (i - j < m.window);
+    case ATTN_MASK_PREFIX_LM: return (j <= i) || (j < m.prefix_len);
+    case ATTN_MASK_DOCUMENT: return (j <= i) && (doc_row[j] == doc_i);
+    default: return false;
+  }
+}
+
+// ALiBi slope of query head hq.
+__device__ __forceinline__ float alibi_slope(const ScoreArgs &s, int hq, int Hq) {
+  if (s.slopes) return s.slopes[hq];
+  return exp2f(-8.0f * (float)(hq + 1) / (float)Hq);
+}
+
+// Coefficient a of the modifier written as a * (j - i): ALIBI a = slope,
+// REL_POS a = -rel_scale (c * (i - j) = -c * (j - i)), NONE a = 0.
+__device__ __forceinline__ float bias_coeff(const ScoreArgs &s, int hq, int Hq) {
+  if (s.kind == ATTN_SCORE_ALIBI) return alibi_slope(s, hq, Hq);
+  if (s.kind == ATTN_SCORE_REL_POS) return -s.rel_scale;
+  return 0.0f;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed (lo = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+}  // namespace attn

@@ -1,0 +1,56 @@
+// Launch interfaces between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include "common.h"
+
+namespace attn {
+
+// Everything the forward kernels read, validated by the host first.
+struct FwdParams {
+  const void *q, *k, *v;
+  void *out;
+  float *lse;
+  int B, Hq, Hkv, Sq, Skv, D;
+  bool out_f32;   // bf16 path: write O as fp32 instead of bf16
+  float scale;
+  MaskArgs mask;
+  ScoreArgs score;
+  // BlockMask (bm_num == nullptr: analytic tile ranges)
+  const int32_t *bm_num;
+  const int32_t *bm_idx;
+  const uint8_t *bm_full;
+  int bm_nqb, bm_nkb, bm_batch, bm_kv_block;
+};
+
+// bf16 MFMA path, D in {64, 128}.
+hipError_t launch_fwd_bf16(const FwdParams &p, hipStream_t stream);
+// fp32 path, D in {16, 32, 64, 128, 256}.
+hipError_t launch_fwd_f32(const FwdParams &p, hipStream_t stream);
+
+struct BlockMaskParams {
+  MaskArgs mask;
+  int B, Sq, Skv, q_block, kv_block, nqb, nkb;
+  int32_t *num;
+  int32_t *idx;
+  uint8_t *full;
+};
+hipError_t launch_block_mask(const BlockMaskParams &p, hipStream_t stream);
+
+struct DecodeParams {
+  const void *q, *k_cache, *v_cache;
+  const int32_t *page_table, *seq_lens;
+  void *out;
+  float *lse;
+  int N, Hq, Hkv, D, page_size, max_pages, num_pages;
+  float scale;
+  ScoreArgs score;
+  float *ws_o;     // [N, Hq, max_splits, D]
+  float *ws_lse;   // [N, Hq, max_splits]
+  int max_splits;
+  int split_pages; // pages per split
+};
+// Split geometry shared by the workspace-size query and the launch.
+void decode_split_geometry(int max_pages, int *split_pages, int *max_splits);
+hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);
+
+}  // namespace attn

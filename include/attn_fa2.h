@@ -1,0 +1,189 @@
+/*
+ * attn_fa2.h — C ABI of the MI355X (gfx950) fused-attention library.
+ *
+ * The operation is softmax attention with a per-score modifier applied before
+ * the softmax and a visibility mask, as stated in the FlexAttention write-up
+ * "新PyTorch API：几行代码实现不同注意力变体，兼具FlashAttention性能和PyTorch
+ * 灵活性" (§FlexAttention: softmax(score_mod(Q·Kᵀ))·V with
+ * score_mod(score, b, h, q_idx, kv_idx)), computed in one pass with an
+ * online softmax (the 1-pass FlashAttention form of "Attention优化｜2w字原理
+ * &图解: 从Online-Softmax到FlashAttention V1/V2/V3", abstract), plus a
+ * block-sparse mask that lets the kernel skip masked key tiles (same
+ * write-up, introduction: exploiting mask sparsity) and a paged-KV decode
+ * (PagedAttention in the write-up's variant list).
+ *
+ * Conventions common to every call:
+ *  - Every tensor pointer is caller-owned DEVICE memory, contiguous,
+ *    row-major, in the layout stated per argument.  The library never
+ *    allocates, frees or keeps a pointer after it returns, and never
+ *    synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and the caller keeps the buffers alive until the stream
+ *    has reached it.
+ *  - Return value: 0 on success, negative on failure:
+ *      ATTN_ERR_INVALID     (-1) a null pointer, a negative or inconsistent size;
+ *      ATTN_ERR_UNSUPPORTED (-2) a valid request outside the supported set;
+ *      ATTN_ERR_LAUNCH      (-3) the HIP runtime rejected a launch;
+ *      ATTN_ERR_WORKSPACE   (-4) the workspace is too small.
+ *    All argument checks run on the host before any launch, so nothing is
+ *    written on error.  A device fault surfaces at the caller's next
+ *    synchronisation (HIP semantics).  attn_last_error() returns a message
+ *    for the last failed call on the calling thread.
+ *  - Indices are raw row / column numbers (the page's score_mod loop runs
+ *    q_idx and kv_idx over positions from 0).
+ */
+#ifndef ATTN_FA2_H
+#define ATTN_FA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID (-1)
+#define ATTN_ERR_UNSUPPORTED (-2)
+#define ATTN_ERR_LAUNCH (-3)
+#define ATTN_ERR_WORKSPACE (-4)
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* Mask predicates (FlexAttention write-up: §Causal Mask, §Sliding Window +
+ * Causal, and the PrefixLM / document-mask entries of its variant list).
+ * visible(b, i, j) for query i, key j:
+ *   NONE      always
+ *   CAUSAL    j <= i
+ *   SLIDING   0 <= i - j < window            (causal + window of `window` keys, self included)
+ *   PREFIX_LM j <= i  or  j < prefix_len
+ *   DOCUMENT  doc_ids[b, i] == doc_ids[b, j]  and  j <= i                      */
+typedef enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_CAUSAL = 1,
+  ATTN_MASK_SLIDING = 2,
+  ATTN_MASK_PREFIX_LM = 3,
+  ATTN_MASK_DOCUMENT = 4
+} attn_mask_kind_t;
+
+typedef struct {
+  int32_t window;          /* SLIDING: number of keys, >= 1 */
+  int32_t prefix_len;      /* PREFIX_LM: bidirectional prefix length, >= 0 */
+  const int32_t *doc_ids;  /* DOCUMENT: device int32 [B, S] (Sq == Skv == S) */
+} attn_mask_params_t;
+
+/* Score modifiers, added to the scaled score before the mask and softmax
+ * (FlexAttention write-up §相对位置编码: a bias from the query-key distance
+ * computed inside the kernel, never stored as an S x S tensor; ALiBi from the
+ * variant list):
+ *   NONE     0
+ *   ALIBI    slope[hq] * (j - i),  slope[h] = 2^(-8 (h+1) / Hq) by default
+ *   REL_POS  rel_scale * (i - j)                                             */
+typedef enum {
+  ATTN_SCORE_NONE = 0,
+  ATTN_SCORE_ALIBI = 1,
+  ATTN_SCORE_REL_POS = 2
+} attn_score_kind_t;
+
+typedef struct {
+  const float *alibi_slopes; /* device float [Hq], or NULL for 2^(-8(h+1)/Hq) */
+  float rel_scale;           /* REL_POS constant c */
+} attn_score_params_t;
+
+/* Block-sparse mask over q_block x kv_block blocks of the Sq x Skv grid (the
+ * last blocks clipped at Sq / Skv).  For batch b (0 when batch == 1, which
+ * broadcasts) and query block qb:
+ *   kv_num_blocks[b, 0, qb]      number of listed key blocks
+ *   kv_indices[b, 0, qb, n]      listed key blocks, ascending; -1 past the count
+ *   kv_full[b, 0, qb, n]         1 if every (i, j) of that block is visible
+ *                                (the kernel then skips the predicate); may be NULL
+ * All device memory; shapes [batch, 1, n_q_blocks(, n_kv_blocks)].          */
+typedef struct {
+  const int32_t *kv_num_blocks;
+  const int32_t *kv_indices;
+  const uint8_t *kv_full;
+  int32_t q_block, kv_block, n_q_blocks, n_kv_blocks, batch;
+} attn_block_mask_t;
+
+/* attn_fwd — fused attention forward, one pass with online softmax.
+ *
+ *   q   [B, Hq,  Sq,  D]   dtype `dt`
+ *   k   [B, Hkv, Skv, D]   dtype `dt`
+ *   v   [B, Hkv, Skv, D]   dtype `dt`
+ *   out [B, Hq,  Sq,  D]   dtype `out_dt` (written): the input dtype, or
+ *                          F32 for bf16 inputs (the fp32 value before the
+ *                          final rounding; a bf16 `out` is exactly that value
+ *                          rounded to nearest even)
+ *   lse [B, Hq,  Sq]       float32, natural-log log-sum-exp of each row's
+ *                          modified scores (written; -inf for a row with no
+ *                          visible key, whose output row is 0)
+ *   Query head hq reads kv head floor(hq * Hkv / Hq) (Hq % Hkv == 0).
+ *   S[i,j] = scale * q_i·k_j + bias(hq, i, j), masked to -inf where not
+ *   visible; out_i = softmax(S[i,:]) · V; lse_i = ln sum_j e^{S[i,j]}.
+ *   bm: NULL iterates the key tiles the mask kind allows analytically;
+ *   otherwise only the listed blocks are visited and the mask predicate is
+ *   evaluated on blocks not flagged full (the caller keeps bm consistent with
+ *   mk: a block left out is treated as fully masked).
+ * Supported: dt = BF16 with D in {64, 128} (MFMA path, fp32 accumulation,
+ * P rounded to bf16 before P·V) or dt = F32 with D in {16, 32, 64, 128, 256}
+ * (fp32 path); bm with q_block == kv_block == 128; DOCUMENT needs
+ * Sq == Skv.  Returns 0 for B, Sq or Hq equal to 0 without launching.     */
+int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+             attn_dtype_t dt, attn_dtype_t out_dt, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+             float scale, attn_mask_kind_t mk, const attn_mask_params_t *mp,
+             attn_score_kind_t sk, const attn_score_params_t *sp,
+             const attn_block_mask_t *bm, void *stream);
+
+/* attn_build_block_mask — BlockMask of mask kind `mk` (same predicate as
+ * attn_fwd) for B x Sq x Skv, in q_block x kv_block blocks.
+ *   kv_num_blocks int32 [B, 1, ceil(Sq/q_block)]                 (written)
+ *   kv_indices    int32 [B, 1, ceil(Sq/q_block), ceil(Skv/kv_block)] (written)
+ *   kv_full       uint8 same shape as kv_indices, or NULL         (written)
+ * Listed: a block holding at least one visible (i, j); full: all visible.
+ * Lists ascend; unused tails are -1 (indices) and 0 (full).  Bit-exact.
+ * Supported: q_block, kv_block in [16, 1024], multiples of 16.             */
+int attn_build_block_mask(attn_mask_kind_t mk, const attn_mask_params_t *mp, int B, int Sq,
+                          int Skv, int q_block, int kv_block, int32_t *kv_num_blocks,
+                          int32_t *kv_indices, uint8_t *kv_full, void *stream);
+
+/* attn_paged_decode_workspace_size — bytes of device scratch attn_paged_decode
+ * needs for this shape (fp32 partial outputs and log-sum-exps of every key
+ * split, sized from max_pages_per_seq so the host never reads seq_lens).   */
+size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int D, int max_pages_per_seq,
+                                        int page_size);
+
+/* attn_paged_decode — one query per sequence against its paged KV cache
+ * (PagedAttention, FlexAttention write-up variant list; the multi-query
+ * paged-attention kernel of "高级特性：探索PyTorch/XLA的Pallas内核和Flash
+ * Attention实现"), split over keys, then merged by log-sum-exp.
+ *   q          [N, Hq, D]                     bf16
+ *   k_cache    [num_pages, Hkv, page_size, D] bf16
+ *   v_cache    [num_pages, Hkv, page_size, D] bf16
+ *   num_pages  pages in the pool; a page id outside [0, num_pages) is read
+ *              as a page of zeros instead of faulting
+ *   page_table int32 [N, max_pages_per_seq]; token t of sequence s sits in
+ *              page page_table[s, t / page_size], slot t % page_size;
+ *              entries past ceil(seq_lens[s] / page_size) are never read
+ *   seq_lens   int32 [N], each in [1, max_pages_per_seq * page_size]
+ *   out        [N, Hq, D] bf16 (written); lse [N, Hq] float32 (written)
+ *   The query of sequence s sits at position seq_lens[s] - 1 and sees every
+ *   key t < seq_lens[s]; ALIBI / REL_POS use i = seq_lens[s] - 1.
+ *   workspace: device scratch of at least
+ *   attn_paged_decode_workspace_size(...) bytes, 256-byte aligned.
+ * Supported: dt = BF16, D == 128, page_size == 16, Hq % Hkv == 0,
+ * Hq / Hkv <= 16.                                                          */
+int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *page_table, const int32_t *seq_lens, void *out, float *lse,
+                      attn_dtype_t dt, int N, int Hq, int Hkv, int D, int page_size,
+                      int max_pages_per_seq, int num_pages, float scale, attn_score_kind_t sk,
+                      const attn_score_params_t *sp, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Message of the last failed call on this thread ("" if none); valid until
+ * the next call on the thread. */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FA2_H */

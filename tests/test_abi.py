@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/attn_fa2.h declares, and rejects bad arguments on the host with the
+documented error codes before any launch (null device pointers are passed, so
+any launch would fault; none happens)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_fa2_fwd_amd as af
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_fa2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(af.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = af.load_library()
+    names = declared_functions()
+    assert names == sorted(af.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _fwd(lib, dt=1, out_dt=None, B=1, Hq=4, Hkv=2, Sq=16, Skv=16, D=64, scale=0.125, mk=0, window=0,
+         prefix=0, sk=0, bm=None, null_score=False):
+    mp = af.MaskParams(window, prefix, None)
+    sp = af.ScoreParams(None, 1.0)
+    out_dt = dt if out_dt is None else out_dt
+    return lib.attn_fwd(None, None, None, None, None, dt, out_dt, B, Hq, Hkv, Sq, Skv, D, scale, mk,
+                        ctypes.byref(mp), sk, None if null_score else ctypes.byref(sp),
+                        ctypes.byref(bm) if bm is not None else None, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(Hq=4, Hkv=3), -1),
+    (dict(Hkv=0), -1),
+    (dict(B=-1), -1),
+    (dict(D=96), -2),
+    (dict(dt=0, D=48), -2),
+    (dict(dt=7), -1),
+    (dict(out_dt=5), -1),
+    (dict(dt=0, out_dt=1), -2),
+    (dict(mk=9), -1),
+    (dict(sk=5), -1),
+    (dict(mk=2, window=0), -1),
+    (dict(mk=3, prefix=-1), -1),
+    (dict(mk=4), -1),                   # DOCUMENT without doc_ids
+    (dict(sk=2, null_score=True), -1),  # REL_POS without params
+    (dict(scale=float("nan")), -1),
+    (dict(), -1),                       # valid shapes but null tensors
+])
+def test_fwd_rejects_bad_arguments(kwargs, code):
+    lib = af.load_library()
+    assert _fwd(lib, **kwargs) == code
+    assert lib.attn_last_error().decode()
+
+
+def test_fwd_block_mask_checks():
+    lib = af.load_library()
+    bm = af.BlockMaskC(None, None, None, 128, 128, 1, 1, 1)
+    assert _fwd(lib, bm=bm) == -1                          # null lists
+    dummy = ctypes.c_int32(0)
+    p = ctypes.addressof(dummy)
+    bm = af.BlockMaskC(p, p, None, 64, 128, 1, 1, 1)
+    assert _fwd(lib, bm=bm) == -2                          # block size
+    bm = af.BlockMaskC(p, p, None, 128, 128, 2, 1, 1)
+    assert _fwd(lib, bm=bm) == -1                          # shape mismatch
+    bm = af.BlockMaskC(p, p, None, 128, 128, 1, 1, 3)
+    assert _fwd(lib, bm=bm) == -1                          # batch mismatch
+
+
+def test_fwd_empty_problem_is_a_no_op():
+    lib = af.load_library()
+    assert _fwd(lib, Sq=0) == 0
+    assert _fwd(lib, B=0) == 0
+
+
+def test_block_mask_builder_checks():
+    lib = af.load_library()
+    mp = af.MaskParams(0, 0, None)
+    assert lib.attn_build_block_mask(1, ctypes.byref(mp), 1, 256, 256, 100, 128, None, None, None, None) == -2
+    assert lib.attn_build_block_mask(1, ctypes.byref(mp), 1, 256, 256, 128, 2048, None, None, None, None) == -2
+    assert lib.attn_build_block_mask(1, ctypes.byref(mp), 1, 256, 256, 128, 128, None, None, None, None) == -1
+    assert lib.attn_build_block_mask(2, ctypes.byref(mp), 1, 256, 256, 128, 128, None, None, None, None) == -1
+    assert lib.attn_build_block_mask(1, ctypes.byref(mp), 0, 256, 256, 128, 128, None, None, None, None) == 0
+
+
+def _dec(lib, N=2, Hq=8, Hkv=2, D=128, page=16, max_pages=4, pool=8, dt=1, sk=0, ws=None, ws_bytes=0):
+    sp = af.ScoreParams(None, 1.0)
+    return lib.attn_paged_decode(None, None, None, None, None, None, None, dt, N, Hq, Hkv, D, page,
+                                 max_pages, pool, 0.1, sk, ctypes.byref(sp), ws, ws_bytes, None)
+
+
+def test_paged_decode_checks():
+    lib = af.load_library()
+    assert _dec(lib, Hq=6, Hkv=4) == -1
+    assert _dec(lib, D=64) == -2
+    assert _dec(lib, page=32) == -2
+    assert _dec(lib, dt=0) == -2
+    assert _dec(lib, Hq=34, Hkv=2) == -2
+    assert _dec(lib, N=0) == 0
+    assert _dec(lib) == -1                                 # null tensors
+    need = lib.attn_paged_decode_workspace_size(2, 8, 128, 4, 16)
+    # rows = N * Hq * ceil(max_pages / 64); O part rounded up to 256 bytes
+    rows = 2 * 8 * 1
+    assert need == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
+    assert lib.attn_paged_decode_workspace_size(0, 8, 128, 4, 16) == 0

@@ -1,0 +1,162 @@
+"""GPU parity of attn_build_block_mask (bit-exact against the oracle) and of
+attn_paged_decode (against the oracle within the bf16 tolerances), through
+the C ABI, including the full-size document and decode workloads."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_fa2_fwd_amd as af
+import oracle
+import workloads
+from gpu_util import announce, compare, f64, requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _ids(lengths, batch=1):
+    return workloads.doc_ids_from_lengths(lengths, batch)
+
+
+BM_CASES = [
+    ("none", 2, 300, 300, 128, 128, dict()),
+    ("causal", 1, 2048, 2048, 128, 128, dict()),
+    ("causal", 2, 300, 517, 64, 32, dict()),
+    ("sliding", 1, 8192, 8192, 128, 128, dict(window=1024)),
+    ("sliding", 1, 1000, 1000, 128, 64, dict(window=37)),
+    ("prefix_lm", 1, 777, 777, 128, 128, dict(prefix_len=300)),
+    ("prefix_lm", 1, 640, 640, 16, 1024, dict(prefix_len=0)),
+    ("document", 2, 1000, 1000, 128, 128, dict(lengths=[300, 1, 129, 127, 443])),
+    ("document", 1, 999, 999, 48, 80, dict(lengths=[10, 500, 489])),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BM_CASES)))
+def test_block_mask_bit_exact(case):
+    mask, B, Sq, Skv, qb, kb, kw = BM_CASES[case]
+    dev = torch.device("cuda")
+    doc = None
+    if mask == "document":
+        doc = torch.from_numpy(_ids(kw["lengths"], B))
+    announce(f"block mask {BM_CASES[case][:6]}")
+    bm = af.attn_build_block_mask(mask, B, Sq, Skv, q_block=qb, kv_block=kb,
+                                  window=kw.get("window", 0), prefix_len=kw.get("prefix_len", 0),
+                                  doc_ids=doc.to(dev) if doc is not None else None, device=dev)
+    torch.cuda.synchronize()
+    ms = oracle.MaskSpec(workloads.MASK_NAMES[mask], window=kw.get("window", 0),
+                         prefix_len=kw.get("prefix_len", 0),
+                         doc_ids=None if doc is None else doc.numpy())
+    num, idx, full = oracle.block_mask_ref(ms, B, Sq, Skv, qb, kb)
+    assert np.array_equal(bm.kv_num_blocks.cpu().numpy(), num)
+    assert np.array_equal(bm.kv_indices.cpu().numpy(), idx)
+    assert np.array_equal(bm.kv_full.cpu().numpy(), full)
+
+
+def test_block_mask_document_workload():
+    w = workloads.DOCUMENT_BLOCKMASK
+    dev = torch.device("cuda")
+    lengths = workloads.doc_lengths(w.Sq, seed=w.seed)
+    doc = torch.from_numpy(_ids(lengths, w.B))
+    announce("block mask document workload")
+    bm = af.attn_build_block_mask("document", w.B, w.Sq, w.Skv, doc_ids=doc.to(dev), device=dev)
+    torch.cuda.synchronize()
+    num, idx, full = oracle.block_mask_ref(oracle.MaskSpec(oracle.MASK_DOCUMENT, doc_ids=doc.numpy()),
+                                           w.B, w.Sq, w.Skv, 128, 128)
+    assert np.array_equal(bm.kv_num_blocks.cpu().numpy(), num)
+    assert np.array_equal(bm.kv_indices.cpu().numpy(), idx)
+    assert np.array_equal(bm.kv_full.cpu().numpy(), full)
+    assert int(num.sum()) == 1348 and int(full.sum()) == 1024
+
+
+# ---------------------------------------------------------------------------
+# paged decode
+
+def small_decode_inputs(lengths, hq=8, hkv=2, max_pages=80, seed=0, poison=False):
+    w = workloads.DecodeWorkload("small", len(lengths), hq, hkv, 128, max_pages=max_pages, seed=seed)
+    inp = workloads.decode_inputs(w, device="cpu", lengths=np.array(lengths))
+    if poison:
+        # NaN in every slot no sequence owns and in the unused tail of the
+        # last page of each sequence; -1 already fills unused table entries
+        owned = torch.zeros(inp["k_cache"].shape[0], 16, dtype=torch.bool)
+        table = inp["page_table"].numpy()
+        for s, L in enumerate(lengths):
+            for t in range(L):
+                owned[table[s, t // 16], t % 16] = True
+        kc, vc = inp["k_cache"], inp["v_cache"]
+        nan = torch.tensor(float("nan"), dtype=torch.bfloat16)
+        for p in range(kc.shape[0]):
+            for slot in range(16):
+                if not owned[p, slot]:
+                    kc[p, :, slot] = nan
+                    vc[p, :, slot] = nan
+    return inp
+
+
+def run_decode(inp, score="none", label="", seqs=None):
+    dev = torch.device("cuda")
+    q = inp["q"]
+    scale = 1.0 / math.sqrt(q.shape[-1])
+    announce(f"paged decode {label} {score}")
+    out, lse = af.attn_paged_decode(q.to(dev), inp["k_cache"].to(dev), inp["v_cache"].to(dev),
+                                    inp["page_table"].to(dev), inp["seq_lens"].to(dev),
+                                    scale=scale, score=score, rel_scale=-0.01)
+    torch.cuda.synchronize()
+    ss = oracle.ScoreSpec(workloads.SCORE_NAMES[score], rel_scale=-0.01)
+    o_ref, l_ref = oracle.paged_decode_ref(f64(q), f64(inp["k_cache"]), f64(inp["v_cache"]),
+                                           inp["page_table"].numpy(), inp["seq_lens"].numpy(),
+                                           scale, ss, seqs=seqs)
+    o = f64(out)
+    l = f64(lse)
+    if seqs is not None:
+        o, l = o[seqs], l[seqs]
+    compare(o, l, o_ref, l_ref, torch.bfloat16, label)
+    return out, lse
+
+
+LENGTHS = [1, 15, 16, 17, 1023, 1024, 1025, 1280]
+
+
+@pytest.mark.parametrize("score", ["none", "alibi", "rel_pos"])
+def test_paged_decode_small(score):
+    run_decode(small_decode_inputs(LENGTHS, seed=1), score, "small")
+
+
+def test_paged_decode_nan_poison_and_gqa_groups():
+    inp = small_decode_inputs([3, 16, 33, 700, 1100], hq=12, hkv=2, seed=2, poison=True)
+    run_decode(inp, "alibi", "poison G=6")
+    inp = small_decode_inputs([5, 64, 300], hq=3, hkv=3, seed=3, poison=True)
+    run_decode(inp, "none", "poison G=1")
+
+
+def test_paged_decode_full_workload_sampled():
+    w = workloads.PAGED_DECODE
+    dev = torch.device("cuda")
+    announce("paged decode full workload: generating")
+    inp = workloads.decode_inputs(w, device=dev)
+    lengths = inp["lengths"]
+    scale = 1.0 / math.sqrt(w.D)
+    announce("paged decode full workload: run")
+    out, lse = af.attn_paged_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
+                                    inp["seq_lens"], scale=scale)
+    out2, lse2 = af.attn_paged_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
+                                      inp["seq_lens"], scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    seqs = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), 0, 31, 63})
+    table = inp["page_table"].cpu().numpy()
+    q = inp["q"].cpu()
+    o_ref = np.zeros((len(seqs), w.Hq, w.D))
+    l_ref = np.zeros((len(seqs), w.Hq))
+    for i, s in enumerate(seqs):
+        L = int(lengths[s])
+        pages = table[s, :(L + 15) // 16]
+        pid = torch.from_numpy(pages.astype(np.int64)).to(dev)
+        kc = inp["k_cache"].index_select(0, pid).cpu()
+        vc = inp["v_cache"].index_select(0, pid).cpu()
+        local = np.arange(len(pages), dtype=np.int32)[None, :]
+        o1, l1 = oracle.paged_decode_ref(f64(q[s:s + 1]), f64(kc), f64(vc), local,
+                                         np.array([L], dtype=np.int32), scale)
+        o_ref[i], l_ref[i] = o1[0], l1[0]
+    compare(f64(out)[seqs], f64(lse)[seqs], o_ref, l_ref, torch.bfloat16, "paged decode full")

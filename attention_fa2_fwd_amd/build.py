@@ -40,13 +40,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the attention library)")
 
 
+# Per-source extra flags.  The forward kernel never produces or consumes NaN
+# (masked scores are -inf, which stays honoured), so max/min need no
+# NaN-quieting of their inputs.
+EXTRA_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, cc: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [cc, *DEVICE_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+    extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+    cmd = [cc, *DEVICE_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(line for line in res.stderr.splitlines()
                     if "packed-fp32-ops" not in line)    # host pass does not know the feature

@@ -83,6 +83,8 @@ int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
     return fail(ATTN_ERR_UNSUPPORTED, "fp32 inputs need an fp32 output");
   if (dt == ATTN_BF16 && D != 64 && D != 128)
     return fail(ATTN_ERR_UNSUPPORTED, "bf16 path supports D in {64, 128} (got %d)", D);
+  if (dt == ATTN_BF16 && (int64_t)Skv * D * 2 > 2147483647LL)
+    return fail(ATTN_ERR_UNSUPPORTED, "bf16 path needs Skv * D * 2 < 2^31 bytes per head");
   if (dt == ATTN_F32 && D != 16 && D != 32 && D != 64 && D != 128 && D != 256)
     return fail(ATTN_ERR_UNSUPPORTED, "fp32 path supports D in {16, 32, 64, 128, 256} (got %d)", D);
   attn::FwdParams p{};

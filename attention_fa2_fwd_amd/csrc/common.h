@@ -75,6 +75,27 @@ __device__ __forceinline__ float bias_coeff(const ScoreArgs &s, int hq, int Hq) 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Max / sum of a value across the two 32-lane halves of a wave64, broadcast
+// to every lane.  v_permlane32_swap exchanges the upper 32 lanes of its first
+// operand with the lower 32 lanes of its second; with two copies of v the
+// operands end up holding [v.lo, v.lo] and [v.hi, v.hi].  Issued as inline
+// asm on two distinct registers: the compiler builtin, given the same value
+// twice, let later code treat the two halves as equal.  The s_nop covers the
+// VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void half_swap(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float half_swap_max(float v) {
+  float a = v, b = v;
+  half_swap(a, b);
+  return __builtin_fmaxf(a, b);
+}
+__device__ __forceinline__ float half_swap_sum(float v) {
+  float a = v, b = v;
+  half_swap(a, b);
+  return a + b;
+}
+
 // Round-to-nearest-even fp32 -> bf16 of two values, packed (lo = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 r = {(__bf16)a, (__bf16)b};

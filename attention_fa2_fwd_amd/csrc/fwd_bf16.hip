@@ -40,6 +40,9 @@ namespace {
 constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // key rows per tile
 constexpr int kThreads = 256;  // 4 waves
+constexpr int kListCap = 512;  // BlockMask entries staged in LDS per query tile
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D>
 struct FwdCfg {
@@ -75,10 +78,15 @@ __device__ __forceinline__ s16x4 lds_read_tr(const __bf16 *p) {
       (__attribute__((address_space(3))) s16x4 *)(p));
 }
 
-template <int D, bool OUT_F32>
+// Compile-time variants: D, the mask kind, GEN (materialise the modified
+// score x = c*s + bias before the max: needed for a bias or a scale <= 0) and
+// the output dtype.  Without GEN the row max is taken on the raw dot products
+// (c > 0 preserves order) and p = 2^(c*s - m) is one FMA and one exp2.
+template <int D, int MASK, bool GEN, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   using C = FwdCfg<D>;
   extern __shared__ __align__(16) __bf16 smem[];
+  __shared__ __align__(16) int32_t kdoc[2][kBN];   // document ids of the staged key tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,19 +111,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   const __bf16 *Kg = a.k + kv_base;
   const __bf16 *Vg = a.v + kv_base;
 
-  // Q^T fragments: lane holds Q[qi][16c + 8h .. 16c + 8h + 7].
+  // Q^T fragments: lane holds Q[qi][16c + 8h .. 16c + 8h + 7] (rows past Sq
+  // read row Sq-1 and are never stored).  The empty asm statements make the
+  // loads complete here, so the tile loop never waits on them.
   bf16x8 qf[C::NDC];
-  if (qi < a.Sq) {
-    const bf16x8 *src = (const bf16x8 *)(a.q + q_base + (size_t)qi * D);
+  {
+    const bf16x8 *src = (const bf16x8 *)(a.q + q_base + (size_t)min(qi, a.Sq - 1) * D);
 #pragma unroll
     for (int c = 0; c < C::NDC; ++c) qf[c] = src[2 * c + h];
-  } else {
 #pragma unroll
-    for (int c = 0; c < C::NDC; ++c) qf[c] = bf16x8{};
+    for (int c = 0; c < C::NDC; ++c) asm volatile("" ::"v"(qf[c]));
   }
 
-  // ---- key tiles to visit
-  const int mk = a.mask.kind;
+  // ---- key tiles to visit.  A BlockMask row is staged in LDS (its first
+  // kListCap entries) so the tile loop reads it without touching the vector
+  // memory counters.
+  __shared__ int32_t s_blk[kListCap];
+  __shared__ uint8_t s_full[kListCap];
   const int qlast = min(q0 + kBM, a.Sq) - 1;
   int n_tiles;
   int t_first = 0;
@@ -126,17 +138,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     const size_t row = (size_t)bb * a.bm_nqb + qt;
     // Counts and indices are device data: clamp them so a malformed list
     // can only drop tiles, never address outside K/V.
-    n_tiles = min(max(a.bm_num[row], 0), a.bm_nkb) * a.tiles_per_block;
+    const int n_blocks = min(max(a.bm_num[row], 0), a.bm_nkb);
+    n_tiles = n_blocks * a.tiles_per_block;
     bm_list = a.bm_idx + row * a.bm_nkb;
     if (a.bm_full) bm_flags = a.bm_full + row * a.bm_nkb;
+    for (int t = tid; t < min(n_blocks, kListCap); t += kThreads) {
+      s_blk[t] = bm_list[t];
+      s_full[t] = bm_flags ? bm_flags[t] : 0;
+    }
+    __syncthreads();   // the list is read by every wave from here on
   } else {
     int lo = 0, hi = a.Skv;
-    if (mk == ATTN_MASK_CAUSAL || mk == ATTN_MASK_DOCUMENT) {
+    if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
       hi = min(a.Skv, qlast + 1);
-    } else if (mk == ATTN_MASK_SLIDING) {
+    } else if (MASK == ATTN_MASK_SLIDING) {
       hi = min(a.Skv, qlast + 1);
       lo = max(0, q0 - a.mask.window + 1);
-    } else if (mk == ATTN_MASK_PREFIX_LM) {
+    } else if (MASK == ATTN_MASK_PREFIX_LM) {
       hi = min(a.Skv, max(qlast + 1, a.mask.prefix_len));
     }
     t_first = lo / kBN;
@@ -144,33 +162,43 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   }
   auto tile_key0 = [&](int n) -> int {
     if (bm_list) {
-      const int blk = bm_list[n / a.tiles_per_block];
+      const int bi = n / a.tiles_per_block;
+      const int blk = (bi < kListCap) ? s_blk[bi] : bm_list[bi];
       if (blk < 0 || blk >= a.bm_nkb) return a.Skv;      // treated as an empty tile
       return blk * (a.tiles_per_block * kBN) + (n % a.tiles_per_block) * kBN;
     }
     return (t_first + n) * kBN;
   };
   auto tile_block_full = [&](int n) -> bool {
-    return bm_flags != nullptr && bm_flags[n / a.tiles_per_block] != 0;
+    if (!bm_flags) return false;
+    const int bi = n / a.tiles_per_block;
+    return ((bi < kListCap) ? s_full[bi] : bm_flags[bi]) != 0;
   };
 
-  // ---- global -> register -> LDS staging of one K/V tile
+  const int32_t *doc_row = (MASK == ATTN_MASK_DOCUMENT) ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride
+                                                        : nullptr;
+
+  // ---- global -> register -> LDS staging of one K/V tile through raw
+  // buffer loads: rows past Skv fall outside the buffer's range and read as
+  // zero, so the ragged last tile needs no branch.
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Kg, (short)0, a.Skv * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Vg, (short)0, a.Skv * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t d_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(doc_row ? doc_row : a.mask.doc_ids), (short)0, doc_row ? a.Skv * 4 : 0, kBufferFlags);
   u32x4 kreg[C::LOADS], vreg[C::LOADS];
+  int32_t dreg = 0;
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int c = i * kThreads + tid;
-      const int row = c / C::CPR;
-      const int col = (c % C::CPR) * 8;
-      const int key = k0 + row;
-      if (key < a.Skv) {
-        kreg[i] = *(const u32x4 *)(Kg + (size_t)key * D + col);
-        vreg[i] = *(const u32x4 *)(Vg + (size_t)key * D + col);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int off = ((k0 + c / C::CPR) * D + (c % C::CPR) * 8) * 2;
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, off, 0, 0);
+      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, off, 0, 0);
     }
+    if (MASK == ATTN_MASK_DOCUMENT && tid < kBN)
+      dreg = __builtin_amdgcn_raw_buffer_load_b32(d_rsrc, (k0 + tid) * 4, 0, 0);
   };
   auto lstore = [&](int buf) {
     __bf16 *Ks = smem + buf * C::STAGE;
@@ -183,21 +211,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
       *(u32x4 *)(Ks + row * C::KS + col) = kreg[i];
       *(u32x4 *)(Vs + row * C::VS + col) = vreg[i];
     }
+    if (MASK == ATTN_MASK_DOCUMENT && tid < kBN) kdoc[buf][tid] = dreg;
   };
 
-  // Per-row softmax state.  m_run: running max of the log2-domain scores
-  // (identical in both lane halves); l_run: this half's share of the row sum.
+  // Per-row softmax state.  m_run: the reference max of the log2-domain
+  // scores (identical in both lane halves), raised only when a tile's max
+  // exceeds it by more than kTau, so p = 2^(x - m_run) <= 2^kTau; l_run: this
+  // half's share of the row sum.
+  constexpr float kTau = 8.0f;
   float m_run = -INFINITY;
   float l_run = 0.0f;
   f32x16 o[C::NDB];
 #pragma unroll
   for (int i = 0; i < C::NDB; ++i) o[i] = f32x16{};
 
-  const float bias2 = bias_coeff(a.score, hq, a.Hq) * kLog2e;
-  const bool has_bias = a.score.kind != ATTN_SCORE_NONE;
-  const int32_t *doc_row = (mk == ATTN_MASK_DOCUMENT) ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride
-                                                      : nullptr;
-  const int doc_i = (doc_row && qi < a.Sq) ? doc_row[qi] : -1;
+  const float c_log2 = a.scale_log2;
+  const float bias2 = GEN ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
+  const int doc_i = (MASK == ATTN_MASK_DOCUMENT) ? doc_row[min(qi, a.Sq - 1)] : 0;
+  asm volatile("" ::"v"(doc_i));   // complete the load before the tile loop
 
   // V^T fragment addressing for ds_read_b64_tr_b16: within each 16-lane
   // group, lanes 4r..4r+3 point at 4 consecutive d of key row r; the read
@@ -221,13 +252,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     // Does this wave have any visible key in the tile, and are all visible?
     bool empty = (qw0 >= a.Sq) || (k0 >= a.Skv);
     bool full = (k0 + kBN <= a.Skv);
-    if (mk == ATTN_MASK_CAUSAL || mk == ATTN_MASK_DOCUMENT) {
+    if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
       empty = empty || (k0 > qw1);
-      full = full && (k0 + kBN - 1 <= qw0) && (mk == ATTN_MASK_CAUSAL || tile_block_full(n));
-    } else if (mk == ATTN_MASK_SLIDING) {
+      full = full && (k0 + kBN - 1 <= qw0);
+      if (MASK == ATTN_MASK_DOCUMENT) full = full && tile_block_full(n);
+    } else if (MASK == ATTN_MASK_SLIDING) {
       empty = empty || (k0 > qw1) || (qw0 - (k0 + kBN - 1) >= a.mask.window);
       full = full && (k0 + kBN - 1 <= qw0) && (qw1 - k0 < a.mask.window);
-    } else if (mk == ATTN_MASK_PREFIX_LM) {
+    } else if (MASK == ATTN_MASK_PREFIX_LM) {
       empty = empty || ((k0 > qw1) && (k0 >= a.mask.prefix_len));
       full = full && ((k0 + kBN - 1 <= qw0) || (k0 + kBN <= a.mask.prefix_len));
     }
@@ -249,46 +281,86 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
         }
       }
 
-      // Modified, masked scores in the log2 domain; tile row max.
-      // Accumulator element r of block kb is key k0 + 32kb + 8(r/4) + 4h + r%4.
+      // Accumulator element r of block kb is key j = jb + kb*32 + 8(r/4) + r%4
+      // with jb = k0 + 4h.
+      const int jb = k0 + 4 * h;
+      if constexpr (GEN) {
+        const float cb = bias2 * (float)(jb - qi);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float off = (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
+            s[kb][r] = __builtin_fmaf(s[kb][r], c_log2, __builtin_fmaf(bias2, off, cb));
+          }
+      }
+      if (!full) {
+        // Partial tile: the mask predicate per element; -inf where hidden
+        // (for the raw scores too: c > 0 on that path).
+        const int dq = qi - jb;                       // j <= qi  <=>  off <= dq
+        int32_t kd[2][4][4];
+        if (MASK == ATTN_MASK_DOCUMENT) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int4 t = *(const int4 *)&kdoc[cur][kb * 32 + 8 * g + 4 * h];
+              kd[kb][g][0] = t.x; kd[kb][g][1] = t.y; kd[kb][g][2] = t.z; kd[kb][g][3] = t.w;
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+            bool vis = off < a.Skv - jb;
+            if (MASK == ATTN_MASK_CAUSAL) vis = vis && (off <= dq);
+            if (MASK == ATTN_MASK_SLIDING) vis = vis && (off <= dq) && (dq - off < a.mask.window);
+            if (MASK == ATTN_MASK_PREFIX_LM) vis = vis && ((off <= dq) || (off < a.mask.prefix_len - jb));
+            if (MASK == ATTN_MASK_DOCUMENT) vis = vis && (off <= dq) && (kd[kb][r >> 2][r & 3] == doc_i);
+            s[kb][r] = vis ? s[kb][r] : -INFINITY;
+          }
+      }
+
+      // Tile row max (raw or modified scores), shared by the two halves.
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * a.scale_log2;
-          const int j = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (has_bias) x += bias2 * (float)(j - qi);
-          if (!full) {
-            const bool vis = (j < a.Skv) && mask_visible(a.mask, qi, j, doc_i, doc_row);
-            x = vis ? x : -INFINITY;
-          }
-          s[kb][r] = x;
-          tmax = fmaxf(tmax, x);
-        }
+        for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[kb][r], s[kb][r + 1]));
+      if constexpr (!GEN) tmax *= c_log2;
+      tmax = half_swap_max(tmax);
+
+      // Raise the reference max only past the threshold (wave-uniform branch).
+      const bool need = tmax > m_run + kTau;
+      if (__any(need)) {
+        const float m_new = need ? tmax : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;   // 0 when m_run = -inf
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::NDB; ++i) o[i] *= alpha;
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < C::NDB; ++i) o[i] *= alpha;
+      const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
 
       // P = 2^(x - m), packed to bf16 pairs in the B-operand order.
       uint32_t pk[2][8];
       float psum = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(s[kb][r] - m_use);
-          const float p1 = fast_exp2(s[kb][r + 1] - m_use);
+          float p0, p1;
+          if constexpr (GEN) {
+            p0 = fast_exp2(s[kb][r] - mu);
+            p1 = fast_exp2(s[kb][r + 1] - mu);
+          } else {
+            p0 = fast_exp2(__builtin_fmaf(s[kb][r], c_log2, -mu));
+            p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c_log2, -mu));
+          }
           psum += p0 + p1;
           pk[kb][r >> 1] = pack_bf16x2(p0, p1);
         }
-      }
       l_run += psum;
 
       // O^T += V^T P^T over four 16-key chunks.
@@ -315,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   }
 
   // ---- epilogue: O / l, LSE = (m + log2 l) ln 2.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_swap_sum(l_run);
   if (qi < a.Sq) {
     const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
     if constexpr (OUT_F32) {
@@ -348,9 +420,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   }
 }
 
-template <int D, bool OUT_F32>
-hipError_t launch_d(const FwdParams &p, hipStream_t stream) {
+template <int D, int MASK, bool GEN, bool OUT_F32>
+hipError_t launch_variant(const KernelArgs &a, unsigned grid, hipStream_t stream) {
   using C = FwdCfg<D>;
+  static bool attr_set = false;  // the attribute is per function; set once
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D, MASK, GEN, OUT_F32>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, GEN, OUT_F32>), dim3(grid), dim3(kThreads),
+                     C::LDS_BYTES, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool GEN, bool OUT_F32>
+hipError_t launch_mask(const KernelArgs &a, int mask, unsigned grid, hipStream_t stream) {
+  switch (mask) {
+    case ATTN_MASK_NONE: return launch_variant<D, ATTN_MASK_NONE, GEN, OUT_F32>(a, grid, stream);
+    case ATTN_MASK_CAUSAL: return launch_variant<D, ATTN_MASK_CAUSAL, GEN, OUT_F32>(a, grid, stream);
+    case ATTN_MASK_SLIDING: return launch_variant<D, ATTN_MASK_SLIDING, GEN, OUT_F32>(a, grid, stream);
+    case ATTN_MASK_PREFIX_LM: return launch_variant<D, ATTN_MASK_PREFIX_LM, GEN, OUT_F32>(a, grid, stream);
+    case ATTN_MASK_DOCUMENT: return launch_variant<D, ATTN_MASK_DOCUMENT, GEN, OUT_F32>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const FwdParams &p, hipStream_t stream) {
   KernelArgs a;
   a.q = (const __bf16 *)p.q;
   a.k = (const __bf16 *)p.k;
@@ -373,23 +471,22 @@ hipError_t launch_d(const FwdParams &p, hipStream_t stream) {
   a.bm_nkb = p.bm_nkb;
   a.bm_batch = p.bm_batch;
   a.tiles_per_block = p.bm_num ? p.bm_kv_block / kBN : 1;
-  static bool attr_set = false;  // per process; the attribute is per function
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D, OUT_F32>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const unsigned grid = (unsigned)(a.n_qtiles * p.B * p.Hq);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, OUT_F32>), dim3(grid), dim3(kThreads), C::LDS_BYTES, stream, a);
-  return hipGetLastError();
+  // The raw-score path needs a positive scale and no bias.
+  const bool gen = (p.score.kind != ATTN_SCORE_NONE) || !(a.scale_log2 > 0.0f);
+  if (gen) {
+    return p.out_f32 ? launch_mask<D, true, true>(a, p.mask.kind, grid, stream)
+                     : launch_mask<D, true, false>(a, p.mask.kind, grid, stream);
+  }
+  return p.out_f32 ? launch_mask<D, false, true>(a, p.mask.kind, grid, stream)
+                   : launch_mask<D, false, false>(a, p.mask.kind, grid, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams &p, hipStream_t stream) {
-  if (p.D == 64) return p.out_f32 ? launch_d<64, true>(p, stream) : launch_d<64, false>(p, stream);
-  if (p.D == 128) return p.out_f32 ? launch_d<128, true>(p, stream) : launch_d<128, false>(p, stream);
+  if (p.D == 64) return launch_d<64>(p, stream);
+  if (p.D == 128) return launch_d<128>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -31,8 +31,18 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
-    """Element-wise comparison against the oracle; returns the error summary."""
+# Relative error of rounding a real number to bf16 (round to nearest even,
+# 8 significant bits): at most half a unit in the last place, 2^-9.
+BF16_ROUND_REL = 2.0 ** -9
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label="", out_rounding=False):
+    """Element-wise comparison against the oracle; returns the error summary.
+
+    out_rounding: the output was rounded to bf16 after the computation; the
+    bound then also admits that final rounding, BF16_ROUND_REL * |O|, on top
+    of the tolerance (the same values before rounding are gated separately at
+    the plain tolerance)."""
     tol = TOL[dtype]
     o = f64(o_gpu) if isinstance(o_gpu, torch.Tensor) else o_gpu
     l = f64(lse_gpu) if isinstance(lse_gpu, torch.Tensor) else lse_gpu
@@ -44,7 +54,12 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
     lerr = np.abs(l[fin] - lse_ref[fin]) if fin.any() else np.zeros(1)
     summary = dict(o_max=float(err.max()), o_mean=float(err.mean()), lse_max=float(lerr.max()))
     print(f"{label}: {summary}", flush=True)
-    assert summary["o_max"] <= tol["o_max"], f"{label}: {summary}"
+    if out_rounding:
+        excess = err - (tol["o_max"] + BF16_ROUND_REL * np.abs(o_ref))
+        summary["o_max_beyond_rounding"] = float(excess.max())
+        assert summary["o_max_beyond_rounding"] <= 0.0, f"{label}: {summary}"
+    else:
+        assert summary["o_max"] <= tol["o_max"], f"{label}: {summary}"
     assert summary["o_mean"] <= tol["o_mean"], f"{label}: {summary}"
     assert summary["lse_max"] <= tol["lse"], f"{label}: {summary}"
     return summary

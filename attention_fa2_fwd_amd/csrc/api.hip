@@ -102,6 +102,8 @@ int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
     if (bm->n_q_blocks != (Sq + 127) / 128 || bm->n_kv_blocks != (Skv + 127) / 128)
       return fail(ATTN_ERR_INVALID, "block mask shape %d x %d does not match Sq=%d Skv=%d",
                   bm->n_q_blocks, bm->n_kv_blocks, Sq, Skv);
+    if (dt == ATTN_BF16 && bm->n_kv_blocks > 1024)
+      return fail(ATTN_ERR_UNSUPPORTED, "block mask with more than 1024 key blocks (Skv > 131072)");
     if (bm->batch != 1 && bm->batch != B)
       return fail(ATTN_ERR_INVALID, "block mask batch %d must be 1 or B=%d", bm->batch, B);
     p.bm_num = bm->kv_num_blocks;

@@ -12,26 +12,40 @@
 //
 // Layout of the work (CDNA4-specific choices):
 //  * workgroup = 256 threads = 4 wave64s, 128 query rows; each wave owns 32
-//    consecutive rows.  Key tiles of 64 rows.  Two workgroups per CU.
+//    consecutive rows.  Key tiles of 64 rows.  Two workgroups per CU, so
+//    each SIMD interleaves two waves: one's MFMAs run beside the other's
+//    softmax.
 //  * Scores are computed transposed, S^T = K·Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand, Q^T (kept in
 //    VGPRs for the whole kernel) the B operand.  In the 32x32 accumulator
 //    layout a lane then holds one query column and 16 keys, so the row max
 //    and row sum of the softmax are in-lane reductions plus one exchange
-//    between the two 32-lane halves, not 32-lane shuffles.
+//    between the two 32-lane halves (v_permlane32_swap).
 //  * P^T leaves the accumulator already in the B-operand layout of the next
 //    MFMA, O^T += V^T·P^T, with the key order inside each 16-key chunk
 //    permuted identically on both operands; V^T fragments are read from the
 //    row-major V tile with ds_read_b64_tr_b16 (the gfx950 transposing LDS
 //    read), so V is never transposed in memory.
-//  * exp2 with scale·log2(e) folded into one multiply; LSE converted to the
-//    natural log on output.
-//  * K/V tiles are double-buffered in LDS; the next tile's global loads are
-//    issued before the current tile's MFMAs.  Rows are padded (K by 16 B, V
-//    by 64 B) so the 16-byte and transposed LDS reads do not collide in banks.
+//  * Software pipeline inside each wave: the S MFMAs of key tile n+1 are
+//    issued before the softmax of tile n, so the matrix cores work while the
+//    VALU computes exp2; K is staged one tile ahead of V.
+//  * K/V tiles move HBM/L2 -> LDS with buffer_load ... lds (no VGPR staging,
+//    rows past Skv read as zero).  A tile is stored as 1 KiB blocks of rows:
+//    key k lives in block k mod NB at slot k / NB, blocks padded apart, so
+//    both the 16-byte K reads and the transposed V reads of a wave hit
+//    distinct banks and every LDS address is a per-lane base plus a
+//    compile-time offset.  The double buffers are four separate LDS
+//    objects named at every access (the tile loop is unrolled by two), so
+//    the compiler sees that reading one buffer does not wait on loads still
+//    landing in another: each wave waits for its loads only at the barrier
+//    that ends the iteration.
+//  * exp2 with scale·log2(e) folded into one FMA; the running max is raised
+//    only when a tile exceeds it by a margin; LSE in natural log on output.
 //  * Causal-type masks: workgroups with the most key tiles are launched
 //    first; waves skip tiles that hold no visible key for their rows and
 //    skip the predicate on tiles where every key is visible.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace attn {
@@ -40,23 +54,25 @@ namespace {
 constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // key rows per tile
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kListCap = 512;  // BlockMask entries staged in LDS per query tile
+constexpr int kListCap = 1024; // BlockMask entries staged in LDS per query tile (host-checked)
 // Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kBufferFlags = 0x00020000;
+constexpr int kKPad = 16;      // bytes between K row blocks
+constexpr int kVPad = 64;      // bytes between V row blocks
 
 template <int D>
 struct FwdCfg {
-  static constexpr int KS = D + 8;    // K row stride in LDS (elements)
-  static constexpr int VS = D + 32;   // V row stride in LDS (elements)
-  static constexpr int KTILE = kBN * KS;
-  static constexpr int VTILE = kBN * VS;
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static constexpr int NDC = D / 16;            // 16-wide d chunks of S^T = K Q^T
-  static constexpr int NDB = D / 32;            // 32-row d blocks of O^T
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int LOADS = kBN * CPR / kThreads;
-  static_assert(kBN * CPR % kThreads == 0, "tile load mapping");
+  static constexpr int ROWB = D * 2;              // bytes of one K/V row
+  static constexpr int NB = kBN * ROWB / 1024;    // 1 KiB row blocks per tile (16 or 8)
+  static constexpr int KBLK = 1024 + kKPad;
+  static constexpr int VBLK = 1024 + kVPad;
+  static constexpr int KTILE = NB * KBLK;         // bytes
+  static constexpr int VTILE = NB * VBLK;
+  static constexpr int NDC = D / 16;              // 16-wide d chunks of S^T = K Q^T
+  static constexpr int NDB = D / 32;              // 32-row d blocks of O^T
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int LOADS = NB / 4;            // direct loads per wave per tile (K or V)
+  static_assert(NB % 4 == 0 && 32 % NB == 0, "block mapping");
 };
 
 struct KernelArgs {
@@ -73,9 +89,10 @@ struct KernelArgs {
   int bm_nqb, bm_nkb, bm_batch, tiles_per_block;
 };
 
-__device__ __forceinline__ s16x4 lds_read_tr(const __bf16 *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(p));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ s16x4 lds_read_tr(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }
 
 // Compile-time variants: D, the mask kind, GEN (materialise the modified
@@ -85,12 +102,21 @@ __device__ __forceinline__ s16x4 lds_read_tr(const __bf16 *p) {
 template <int D, int MASK, bool GEN, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   using C = FwdCfg<D>;
-  extern __shared__ __align__(16) __bf16 smem[];
-  __shared__ __align__(16) int32_t kdoc[2][kBN];   // document ids of the staged key tiles
+  // K and V double buffers as four distinct LDS objects, always addressed
+  // through their own names: the compiler can then tell that reading one
+  // buffer does not depend on buffer->LDS loads still in flight to another,
+  // and does not wait for them (the barriers below order the buffers).
+  __shared__ __align__(16) char k_lds0[C::KTILE];
+  __shared__ __align__(16) char k_lds1[C::KTILE];
+  __shared__ __align__(16) char v_lds0[C::VTILE];
+  __shared__ __align__(16) char v_lds1[C::VTILE];
+  __shared__ __align__(16) int32_t kdoc[3][kBN];   // document ids of staged key tiles
+  __shared__ int32_t s_blk[kListCap];
+  __shared__ uint8_t s_full[kListCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = tid >> 6;   // kept per-lane: branches on it stay exec-masked, which keeps the schedule tight
   const int h = lane >> 5;      // lane half: selects keys 4h..4h+3 of each 8
   const int l32 = lane & 31;    // query column of this lane
 
@@ -108,8 +134,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
 
   const size_t q_base = ((size_t)(b * a.Hq + hq) * a.Sq) * D;
   const size_t kv_base = ((size_t)(b * a.Hkv + hkv) * a.Skv) * D;
-  const __bf16 *Kg = a.k + kv_base;
-  const __bf16 *Vg = a.v + kv_base;
 
   // Q^T fragments: lane holds Q[qi][16c + 8h .. 16c + 8h + 7] (rows past Sq
   // read row Sq-1 and are never stored).  The empty asm statements make the
@@ -123,11 +147,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     for (int c = 0; c < C::NDC; ++c) asm volatile("" ::"v"(qf[c]));
   }
 
-  // ---- key tiles to visit.  A BlockMask row is staged in LDS (its first
-  // kListCap entries) so the tile loop reads it without touching the vector
-  // memory counters.
-  __shared__ int32_t s_blk[kListCap];
-  __shared__ uint8_t s_full[kListCap];
+  // ---- key tiles to visit.  A BlockMask row is staged in LDS so the tile
+  // loop reads it without vector memory waits (the host limits a row to
+  // kListCap entries).
   const int qlast = min(q0 + kBM, a.Sq) - 1;
   int n_tiles;
   int t_first = 0;
@@ -138,11 +160,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     const size_t row = (size_t)bb * a.bm_nqb + qt;
     // Counts and indices are device data: clamp them so a malformed list
     // can only drop tiles, never address outside K/V.
-    const int n_blocks = min(max(a.bm_num[row], 0), a.bm_nkb);
+    const int n_blocks = min(max(a.bm_num[row], 0), min(a.bm_nkb, kListCap));
     n_tiles = n_blocks * a.tiles_per_block;
     bm_list = a.bm_idx + row * a.bm_nkb;
     if (a.bm_full) bm_flags = a.bm_full + row * a.bm_nkb;
-    for (int t = tid; t < min(n_blocks, kListCap); t += kThreads) {
+    for (int t = tid; t < n_blocks; t += kThreads) {
       s_blk[t] = bm_list[t];
       s_full[t] = bm_flags ? bm_flags[t] : 0;
     }
@@ -160,59 +182,71 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     t_first = lo / kBN;
     n_tiles = (hi > lo) ? (hi + kBN - 1) / kBN - t_first : 0;
   }
-  auto tile_key0 = [&](int n) -> int {
+  auto tile_key0 = [&](int n) __attribute__((always_inline)) -> int {
     if (bm_list) {
       const int bi = n / a.tiles_per_block;
-      const int blk = (bi < kListCap) ? s_blk[bi] : bm_list[bi];
+      const int blk = s_blk[bi];   // bi < n_blocks <= kListCap
       if (blk < 0 || blk >= a.bm_nkb) return a.Skv;      // treated as an empty tile
       return blk * (a.tiles_per_block * kBN) + (n % a.tiles_per_block) * kBN;
     }
     return (t_first + n) * kBN;
   };
-  auto tile_block_full = [&](int n) -> bool {
+  auto tile_block_full = [&](int n) __attribute__((always_inline)) -> bool {
     if (!bm_flags) return false;
     const int bi = n / a.tiles_per_block;
-    return ((bi < kListCap) ? s_full[bi] : bm_flags[bi]) != 0;
+    return s_full[bi] != 0;
   };
 
   const int32_t *doc_row = (MASK == ATTN_MASK_DOCUMENT) ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride
                                                         : nullptr;
 
-  // ---- global -> register -> LDS staging of one K/V tile through raw
-  // buffer loads: rows past Skv fall outside the buffer's range and read as
-  // zero, so the ragged last tile needs no branch.
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void *)Kg, (short)0, a.Skv * D * 2, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void *)Vg, (short)0, a.Skv * D * 2, kBufferFlags);
+  // ---- HBM/L2 -> LDS through buffer_load ... lds.  Wave w, load i fills
+  // row block blk = 4i + w: lane L writes bytes [16L, 16L + 16) of the block,
+  // i.e. slot L / CPR (key blk + NB * slot), 16-byte chunk L % CPR.  Keys
+  // past Skv fall outside the buffer's range and read as zero.
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.k + kv_base), (short)0, a.Skv * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.v + kv_base), (short)0, a.Skv * D * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t d_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(doc_row ? doc_row : a.mask.doc_ids), (short)0, doc_row ? a.Skv * 4 : 0, kBufferFlags);
-  u32x4 kreg[C::LOADS], vreg[C::LOADS];
-  int32_t dreg = 0;
-  auto gload = [&](int k0) {
+  // Byte offset of this lane's chunk for load i = 0; load i is 4 rows
+  // further on.  key0 is wave-uniform; on the BlockMask path it comes from
+  // LDS, so it is moved to a scalar register explicitly (it is the loads'
+  // scalar offset).
+  const int ld_off = ((wave + C::NB * (lane / C::CPR)) * D + (lane % C::CPR) * 8) * 2;
+  auto load_k = [&](char *dst, int key0) __attribute__((always_inline)) {
+    const int soff = __builtin_amdgcn_readfirstlane(key0 * D * 2);
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int c = i * kThreads + tid;
-      const int off = ((k0 + c / C::CPR) * D + (c % C::CPR) * 8) * 2;
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, off, 0, 0);
-      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, off, 0, 0);
-    }
-    if (MASK == ATTN_MASK_DOCUMENT && tid < kBN)
-      dreg = __builtin_amdgcn_raw_buffer_load_b32(d_rsrc, (k0 + tid) * 4, 0, 0);
+    for (int i = 0; i < C::LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void *)(dst + (4 * i + wave) * C::KBLK), 16,
+                                               ld_off + i * (4 * D * 2), soff, 0, 0);
   };
-  auto lstore = [&](int buf) {
-    __bf16 *Ks = smem + buf * C::STAGE;
-    __bf16 *Vs = Ks + C::KTILE;
+  auto load_v = [&](char *dst, int key0) __attribute__((always_inline)) {
+    const int soff = __builtin_amdgcn_readfirstlane(key0 * D * 2);
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int c = i * kThreads + tid;
-      const int row = c / C::CPR;
-      const int col = (c % C::CPR) * 8;
-      *(u32x4 *)(Ks + row * C::KS + col) = kreg[i];
-      *(u32x4 *)(Vs + row * C::VS + col) = vreg[i];
-    }
-    if (MASK == ATTN_MASK_DOCUMENT && tid < kBN) kdoc[buf][tid] = dreg;
+    for (int i = 0; i < C::LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void *)(dst + (4 * i + wave) * C::VBLK), 16,
+                                               ld_off + i * (4 * D * 2), soff, 0, 0);
   };
+  // Document ids of a key tile go through wave 0's registers into kdoc (a
+  // plain LDS store, so later reads of kdoc never wait for the buffer->LDS
+  // loads): fetched at the start of an iteration, stored at its end.
+  auto load_doc = [&](int key0) __attribute__((always_inline)) -> int {
+    return __builtin_amdgcn_raw_buffer_load_b32(d_rsrc, lane * 4, __builtin_amdgcn_readfirstlane(key0 * 4), 0);
+  };
+
+  // Per-lane LDS read bases.  K (A operand of S^T): key kb*32 + l32, bytes
+  // of chunk 2c + h.  V^T (ds_read_b64_tr_b16): within each 16-lane group,
+  // lanes 4r..4r+3 point at 4 consecutive d of key 4h + r (+16c, +8 for the
+  // second read); the read hands lane i the 4 keys' values at d = i.
+  // Key kk + x with x = the lane's part lives at block (kk % NB) + x % NB:
+  // the compile-time parts below never carry (kk % NB + x < NB).
+  const int k_rd = (l32 % C::NB) * C::KBLK + (l32 / C::NB) * C::ROWB + h * 16;
+  const int tr_j = lane & 15;
+  const int tr_key = 4 * h + (tr_j >> 2);
+  const int v_rd = tr_key * C::VBLK + (16 * ((lane >> 4) & 1) + 4 * (tr_j & 3)) * 2;
+  constexpr auto v_key_off = [](int kk) { return (kk % C::NB) * C::VBLK + (kk / C::NB) * C::ROWB; };
 
   // Per-row softmax state.  m_run: the reference max of the log2-domain
   // scores (identical in both lane halves), raised only when a tile's max
@@ -230,161 +264,224 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   const int doc_i = (MASK == ATTN_MASK_DOCUMENT) ? doc_row[min(qi, a.Sq - 1)] : 0;
   asm volatile("" ::"v"(doc_i));   // complete the load before the tile loop
 
-  // V^T fragment addressing for ds_read_b64_tr_b16: within each 16-lane
-  // group, lanes 4r..4r+3 point at 4 consecutive d of key row r; the read
-  // hands lane i the 4 keys' values at d = i.
-  const int tr_g = lane >> 4;
-  const int tr_j = lane & 15;
-  const int tr_key = 4 * h + (tr_j >> 2);                 // + 16c (+8 for the second read)
-  const int tr_d = 16 * (tr_g & 1) + 4 * (tr_j & 3);      // + 32 dblk
+  // Visibility class of a key tile for this wave.
+  auto tile_empty = [&](int k0) __attribute__((always_inline)) -> bool {
+    bool e = (qw0 >= a.Sq) || (k0 >= a.Skv);
+    if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) e = e || (k0 > qw1);
+    if (MASK == ATTN_MASK_SLIDING) e = e || (k0 > qw1) || (qw0 - (k0 + kBN - 1) >= a.mask.window);
+    if (MASK == ATTN_MASK_PREFIX_LM) e = e || ((k0 > qw1) && (k0 >= a.mask.prefix_len));
+    return e;
+  };
+  auto tile_full = [&](int k0, int n) __attribute__((always_inline)) -> bool {
+    bool f = (k0 + kBN <= a.Skv);
+    if (MASK == ATTN_MASK_CAUSAL) f = f && (k0 + kBN - 1 <= qw0);
+    if (MASK == ATTN_MASK_DOCUMENT) f = f && (k0 + kBN - 1 <= qw0) && tile_block_full(n);
+    if (MASK == ATTN_MASK_SLIDING) f = f && (k0 + kBN - 1 <= qw0) && (qw1 - k0 < a.mask.window);
+    if (MASK == ATTN_MASK_PREFIX_LM) f = f && ((k0 + kBN - 1 <= qw0) || (k0 + kBN <= a.mask.prefix_len));
+    return f;
+  };
 
+  // S^T = K Q^T for the two 32-key blocks of the K tile at kt.
+  auto compute_s = [&](f32x16 (&s)[2], const char *kt) __attribute__((always_inline)) {
+    const char *kbase = kt + k_rd;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < C::NDC; ++c) {
+        const bf16x8 ka = *(const bf16x8 *)(kbase + (32 * kb / C::NB) * C::ROWB + 32 * c);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], s[kb], 0, 0, 0);
+      }
+    }
+  };
+
+  // Head of the softmax of one tile (scores s, first key k0, index n): bias,
+  // mask, tile max, threshold rescale of O and l.  Returns the exponent
+  // reference mu.
+  auto softmax_head = [&](f32x16 (&s)[2], int k0, int n, int dslot) __attribute__((always_inline)) -> float {
+    const bool full = tile_full(k0, n);
+    // Accumulator element r of block kb is key j = jb + kb*32 + 8(r/4) + r%4
+    // with jb = k0 + 4h.
+    const int jb = k0 + 4 * h;
+    if constexpr (GEN) {
+      const float cb = bias2 * (float)(jb - qi);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float off = (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
+          s[kb][r] = __builtin_fmaf(s[kb][r], c_log2, __builtin_fmaf(bias2, off, cb));
+        }
+    }
+    if (!full) {
+      // Partial tile: the mask predicate per element; -inf where hidden (for
+      // the raw scores too: c > 0 on that path).
+      const int dq = qi - jb;                       // j <= qi  <=>  off <= dq
+      int32_t kd[2][4][4];
+      if (MASK == ATTN_MASK_DOCUMENT) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int4 t = *(const int4 *)&kdoc[dslot][kb * 32 + 8 * g + 4 * h];
+            kd[kb][g][0] = t.x; kd[kb][g][1] = t.y; kd[kb][g][2] = t.z; kd[kb][g][3] = t.w;
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          bool vis = off < a.Skv - jb;
+          if (MASK == ATTN_MASK_CAUSAL) vis = vis && (off <= dq);
+          if (MASK == ATTN_MASK_SLIDING) vis = vis && (off <= dq) && (dq - off < a.mask.window);
+          if (MASK == ATTN_MASK_PREFIX_LM) vis = vis && ((off <= dq) || (off < a.mask.prefix_len - jb));
+          if (MASK == ATTN_MASK_DOCUMENT) vis = vis && (off <= dq) && (kd[kb][r >> 2][r & 3] == doc_i);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+        }
+    }
+
+    // Tile row max (raw or modified scores), shared by the two halves.  Four
+    // independent partial maxima keep the dependency chain short.
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        mx[(r >> 1) & 3] = __builtin_fmaxf(mx[(r >> 1) & 3], __builtin_fmaxf(s[kb][r], s[kb][r + 1]));
+    float tmax = __builtin_fmaxf(__builtin_fmaxf(mx[0], mx[1]), __builtin_fmaxf(mx[2], mx[3]));
+    if constexpr (!GEN) tmax *= c_log2;
+    tmax = half_swap_max(tmax);
+
+    // Raise the reference max only past the threshold (wave-uniform branch).
+    const bool need = tmax > m_run + kTau;
+    if (__any(need)) {
+      const float m_new = need ? tmax : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;   // 0 when m_run = -inf
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < C::NDB; ++i) o[i] *= alpha;
+    }
+    return (m_run == -INFINITY) ? 0.0f : m_run;
+  };
+
+  // Tail of the softmax: P = 2^(x - mu) and O^T += V^T P^T (V in buffer
+  // tile vt), one 16-key chunk at a time, each chunk's P·V MFMAs right after its
+  // exp2s.  With WITH_S the S MFMAs of the next tile (K tile kt) are
+  // spread over the chunks: one straight-line region in which the matrix
+  // cores and the VALU work side by side.
+  auto softmax_tail = [&](auto with_s, f32x16 (&s)[2], float mu, const char *vt, f32x16 (&sn)[2],
+                          const char *kt) __attribute__((always_inline)) {
+    constexpr bool WITH_S = decltype(with_s)::value;
+    constexpr int S_PER_CHUNK = 2 * C::NDC / 4;       // S MFMAs per 16-key chunk
+    const char *vbase = vt + v_rd;
+    const char *kbase = kt + k_rd;
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // independent partial row sums
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // Keep each chunk's LDS reads in the chunk: hoisted further they would
+      // only hold registers longer.
+      asm volatile("" ::: "memory");
+      if constexpr (WITH_S) {
+#pragma unroll
+        for (int t = 0; t < S_PER_CHUNK; ++t) {
+          const int i = c * S_PER_CHUNK + t;
+          const int kb = i / C::NDC, cc = i % C::NDC;
+          const bf16x8 ka = *(const bf16x8 *)(kbase + (32 * kb / C::NB) * C::ROWB + 32 * cc);
+          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[cc], cc == 0 ? f32x16{} : sn[kb],
+                                                           0, 0, 0);
+        }
+      }
+      const int kb = c >> 1;
+      const int r0 = 8 * (c & 1);
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float p0, p1;
+        if constexpr (GEN) {
+          p0 = fast_exp2(s[kb][r0 + e] - mu);
+          p1 = fast_exp2(s[kb][r0 + e + 1] - mu);
+        } else {
+          p0 = fast_exp2(__builtin_fmaf(s[kb][r0 + e], c_log2, -mu));
+          p1 = fast_exp2(__builtin_fmaf(s[kb][r0 + e + 1], c_log2, -mu));
+        }
+        ps[e >> 1] += p0 + p1;
+        pw[e >> 1] = pack_bf16x2(p0, p1);
+      }
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const s16x4 lo = lds_read_tr(vbase + v_key_off(16 * c) + 64 * db);
+        const s16x4 hi = lds_read_tr(vbase + v_key_off(16 * c + 8) + 64 * db);
+        const u32x4 vw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pb,
+                                                        o[db], 0, 0, 0);
+      }
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+
+  // ---- prologue: K0, V0, K1 (and the document ids of tiles 0, 1)
+  // resident; S0 computed.  Tile n uses K and V buffer n % 2 and document
+  // slot n % 3.
+  f32x16 sa[2], sb[2];
   if (n_tiles > 0) {
-    gload(tile_key0(0));
-    lstore(0);
+    load_k(k_lds0, tile_key0(0));
+    load_v(v_lds0, tile_key0(0));
+    if (n_tiles > 1) load_k(k_lds1, tile_key0(1));
+    if (MASK == ATTN_MASK_DOCUMENT && wave == 0) {
+      kdoc[0][lane] = load_doc(tile_key0(0));
+      if (n_tiles > 1) kdoc[1][lane] = load_doc(tile_key0(1));
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0)
   }
   __syncthreads();
+  if (n_tiles > 0 && !tile_empty(tile_key0(0))) compute_s(sa, k_lds0);
+  // Iteration 0 refills K buffer 0 (tile 2): every wave must be done reading
+  // tile 0 from it first.  Later refills target a buffer last read before
+  // the previous iteration's barrier.
+  __syncthreads();
 
-  for (int n = 0; n < n_tiles; ++n) {
-    const int cur = n & 1;
+  // ---- tile loop, unrolled by two so that the S accumulators alternate and
+  // every LDS access names its buffer.
+  // Iteration n: (1) start loading K[n+2] and V[n+1] into the buffers tile
+  // n-1 freed (k_fill, v_fill) and fetch the document ids of tile n+2;
+  // (2) softmax of tile n with its P·V MFMAs (V tile v_cur), interleaved with
+  // the S MFMAs of tile n+1 (K tile k_next); (3) store the ids into the slot
+  // tile n-1 freed, wait for this wave's loads, barrier.
+  auto iteration = [&](int n, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], char *k_fill, char *v_fill,
+                       const char *v_cur, const char *k_next) __attribute__((always_inline)) {
     const int k0 = tile_key0(n);
-    if (n + 1 < n_tiles) gload(tile_key0(n + 1));
-
-    // Does this wave have any visible key in the tile, and are all visible?
-    bool empty = (qw0 >= a.Sq) || (k0 >= a.Skv);
-    bool full = (k0 + kBN <= a.Skv);
-    if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
-      empty = empty || (k0 > qw1);
-      full = full && (k0 + kBN - 1 <= qw0);
-      if (MASK == ATTN_MASK_DOCUMENT) full = full && tile_block_full(n);
-    } else if (MASK == ATTN_MASK_SLIDING) {
-      empty = empty || (k0 > qw1) || (qw0 - (k0 + kBN - 1) >= a.mask.window);
-      full = full && (k0 + kBN - 1 <= qw0) && (qw1 - k0 < a.mask.window);
-    } else if (MASK == ATTN_MASK_PREFIX_LM) {
-      empty = empty || ((k0 > qw1) && (k0 >= a.mask.prefix_len));
-      full = full && ((k0 + kBN - 1 <= qw0) || (k0 + kBN <= a.mask.prefix_len));
+    int doc_fill = 0;
+    if (n + 2 < n_tiles) {
+      if (MASK == ATTN_MASK_DOCUMENT && wave == 0) doc_fill = load_doc(tile_key0(n + 2));
+      load_k(k_fill, tile_key0(n + 2));
     }
-
-    if (!empty) {
-      const __bf16 *Ks = smem + cur * C::STAGE;
-      const __bf16 *Vs = Ks + C::KTILE;
-
-      // S^T = K Q^T for two 32-key blocks.
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const __bf16 *krow = Ks + (kb * 32 + l32) * C::KS + 8 * h;
-#pragma unroll
-        for (int c = 0; c < C::NDC; ++c) {
-          const bf16x8 ka = *(const bf16x8 *)(krow + 16 * c);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], s[kb], 0, 0, 0);
-        }
-      }
-
-      // Accumulator element r of block kb is key j = jb + kb*32 + 8(r/4) + r%4
-      // with jb = k0 + 4h.
-      const int jb = k0 + 4 * h;
-      if constexpr (GEN) {
-        const float cb = bias2 * (float)(jb - qi);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float off = (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
-            s[kb][r] = __builtin_fmaf(s[kb][r], c_log2, __builtin_fmaf(bias2, off, cb));
-          }
-      }
-      if (!full) {
-        // Partial tile: the mask predicate per element; -inf where hidden
-        // (for the raw scores too: c > 0 on that path).
-        const int dq = qi - jb;                       // j <= qi  <=>  off <= dq
-        int32_t kd[2][4][4];
-        if (MASK == ATTN_MASK_DOCUMENT) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int4 t = *(const int4 *)&kdoc[cur][kb * 32 + 8 * g + 4 * h];
-              kd[kb][g][0] = t.x; kd[kb][g][1] = t.y; kd[kb][g][2] = t.z; kd[kb][g][3] = t.w;
-            }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-            bool vis = off < a.Skv - jb;
-            if (MASK == ATTN_MASK_CAUSAL) vis = vis && (off <= dq);
-            if (MASK == ATTN_MASK_SLIDING) vis = vis && (off <= dq) && (dq - off < a.mask.window);
-            if (MASK == ATTN_MASK_PREFIX_LM) vis = vis && ((off <= dq) || (off < a.mask.prefix_len - jb));
-            if (MASK == ATTN_MASK_DOCUMENT) vis = vis && (off <= dq) && (kd[kb][r >> 2][r & 3] == doc_i);
-            s[kb][r] = vis ? s[kb][r] : -INFINITY;
-          }
-      }
-
-      // Tile row max (raw or modified scores), shared by the two halves.
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[kb][r], s[kb][r + 1]));
-      if constexpr (!GEN) tmax *= c_log2;
-      tmax = half_swap_max(tmax);
-
-      // Raise the reference max only past the threshold (wave-uniform branch).
-      const bool need = tmax > m_run + kTau;
-      if (__any(need)) {
-        const float m_new = need ? tmax : m_run;
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;   // 0 when m_run = -inf
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < C::NDB; ++i) o[i] *= alpha;
-      }
-      const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
-
-      // P = 2^(x - m), packed to bf16 pairs in the B-operand order.
-      uint32_t pk[2][8];
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float p0, p1;
-          if constexpr (GEN) {
-            p0 = fast_exp2(s[kb][r] - mu);
-            p1 = fast_exp2(s[kb][r + 1] - mu);
-          } else {
-            p0 = fast_exp2(__builtin_fmaf(s[kb][r], c_log2, -mu));
-            p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c_log2, -mu));
-          }
-          psum += p0 + p1;
-          pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-        }
-      l_run += psum;
-
-      // O^T += V^T P^T over four 16-key chunks.
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 pw = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1],
-                          pk[c >> 1][4 * (c & 1) + 2], pk[c >> 1][4 * (c & 1) + 3]};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        const __bf16 *vbase = Vs + (16 * c + tr_key) * C::VS + tr_d;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const s16x4 lo = lds_read_tr(vbase + 32 * db);
-          const s16x4 hi = lds_read_tr(vbase + 8 * C::VS + 32 * db);
-          const u32x4 vw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pb,
-                                                          o[db], 0, 0, 0);
-        }
-      }
+    if (n + 1 < n_tiles) load_v(v_fill, tile_key0(n + 1));
+    const bool cur_live = !tile_empty(k0);
+    const bool next_live = (n + 1 < n_tiles) && !tile_empty(tile_key0(n + 1));
+    if (cur_live) {
+      // The next tile's S is computed whether or not that tile is live for
+      // this wave (a dead or absent tile reads a stale, valid K buffer and
+      // the result is never used): one code path keeps the whole tail in a
+      // single scheduling region.
+      const float mu = softmax_head(s_cur, k0, n, n % 3);
+      softmax_tail(std::true_type{}, s_cur, mu, v_cur, s_next, k_next);
+    } else if (next_live) {
+      compute_s(s_next, k_next);
     }
-
-    if (n + 1 < n_tiles) lstore(cur ^ 1);
+    if (MASK == ATTN_MASK_DOCUMENT && wave == 0 && n + 2 < n_tiles) kdoc[(n + 2) % 3][lane] = doc_fill;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads and LDS stores are done
     __syncthreads();
+  };
+  int n = 0;
+  for (; n + 1 < n_tiles; n += 2) {
+    iteration(n, sa, sb, k_lds0, v_lds1, v_lds0, k_lds1);
+    iteration(n + 1, sb, sa, k_lds1, v_lds0, v_lds1, k_lds0);
   }
+  if (n < n_tiles) iteration(n, sa, sb, k_lds0, v_lds1, v_lds0, k_lds1);
 
   // ---- epilogue: O / l, LSE = (m + log2 l) ln 2.
   const float l_tot = half_swap_sum(l_run);
@@ -422,16 +519,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
 
 template <int D, int MASK, bool GEN, bool OUT_F32>
 hipError_t launch_variant(const KernelArgs &a, unsigned grid, hipStream_t stream) {
-  using C = FwdCfg<D>;
-  static bool attr_set = false;  // the attribute is per function; set once
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D, MASK, GEN, OUT_F32>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, GEN, OUT_F32>), dim3(grid), dim3(kThreads),
-                     C::LDS_BYTES, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, GEN, OUT_F32>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

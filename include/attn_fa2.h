@@ -125,7 +125,8 @@ typedef struct {
  *   mk: a block left out is treated as fully masked).
  * Supported: dt = BF16 with D in {64, 128} (MFMA path, fp32 accumulation,
  * P rounded to bf16 before P·V) or dt = F32 with D in {16, 32, 64, 128, 256}
- * (fp32 path); bm with q_block == kv_block == 128; DOCUMENT needs
+ * (fp32 path); bm with q_block == kv_block == 128 (and, on the bf16 path,
+ * at most 1024 key blocks, Skv <= 131072); DOCUMENT needs
  * Sq == Skv.  Returns 0 for B, Sq or Hq equal to 0 without launching.     */
 int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
              attn_dtype_t dt, attn_dtype_t out_dt, int B, int Hq, int Hkv, int Sq, int Skv, int D,

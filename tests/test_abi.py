@@ -77,6 +77,11 @@ def test_fwd_block_mask_checks():
     assert _fwd(lib, bm=bm) == -1                          # shape mismatch
     bm = af.BlockMaskC(p, p, None, 128, 128, 1, 1, 3)
     assert _fwd(lib, bm=bm) == -1                          # batch mismatch
+    # The bf16 kernel stages one row of the block list in LDS: at most 1024
+    # key blocks (Skv <= 131072); the fp32 path has no such limit.
+    bm = af.BlockMaskC(p, p, None, 128, 128, 1, 1025, 1)
+    assert _fwd(lib, Sq=16, Skv=1025 * 128, bm=bm) == -2
+    assert "1024" in lib.attn_last_error().decode()
 
 
 def test_fwd_empty_problem_is_a_no_op():

@@ -242,26 +242,39 @@ def main():
     lse_c = torch.empty_like(lse_d)
     scale = 1.0 / math.sqrt(wd.D)
 
-    def step(ev=None):
+    def dense():
         af.attn_fwd(q, k, v, scale=scale, mask="none", out=out_d, lse=lse_d)
-        if ev is not None:
-            ev.append(Timer(torch).event())
+
+    def causal():
         af.attn_fwd(q, k, v, scale=scale, mask="causal", out=out_c, lse=lse_c)
-        if ev is not None:
-            ev.append(Timer(torch).event())
 
     for _ in range(args.warmup):
-        step()
+        dense()
+        causal()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-    events = [Timer(torch).event()]
+    t = Timer(torch)
+    e0 = t.event()
     for _ in range(args.steps):
-        step(events)
+        dense()
+        causal()
+    e1 = t.event()
     torch.cuda.synchronize()
-    total_ms = events[0].elapsed_time(events[-1])
-    ms_step = total_ms / args.steps
-    dense_ms = sum(events[2 * i].elapsed_time(events[2 * i + 1]) for i in range(args.steps)) / args.steps
-    causal_ms = sum(events[2 * i + 1].elapsed_time(events[2 * i + 2]) for i in range(args.steps)) / args.steps
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # Launch duration of each kernel variant: the same launch back to back
+    # between two events on the launch stream, so the figure is the kernel's
+    # own time (the launches queue ahead of the GPU).
+    def launch_ms(fn):
+        a0 = t.event()
+        for _ in range(args.steps):
+            fn()
+        a1 = t.event()
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / args.steps
+
+    dense_ms = launch_ms(dense)
+    causal_ms = launch_ms(causal)
     S = wd.Sq
     f_dense = 4.0 * wd.D * wd.B * wd.Hq * S * S
     f_causal = 4.0 * wd.D * wd.B * wd.Hq * S * (S + 1) // 2

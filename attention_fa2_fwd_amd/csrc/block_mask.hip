@@ -13,11 +13,13 @@
 //              all: q0 - k1 >= 0 && q1 - k0 < W
 //   PREFIX_LM  any: k0 <= q1 || k0 < P        all: k1 < max(P, q0 + 1)
 //   NONE       any and all
-// DOCUMENT compares document ids element by element (no ordering of the ids
-// is assumed), after rejecting blocks that lie wholly above the diagonal.
+// DOCUMENT decides a block from the ids' summary where it can (blocks wholly
+// above the diagonal, blocks that straddle it, id ranges that do not meet,
+// blocks holding a single id) and otherwise scans for a shared id; no
+// ordering of the ids is assumed.
 //
-// One workgroup per (batch, query block); the list is compacted with wave
-// ballots, 256 key blocks at a time.
+// One workgroup per (batch, query block), one key block per thread; the list
+// is compacted with wave ballots, 256 key blocks at a time.
 #include "kernels.h"
 
 namespace attn {
@@ -49,9 +51,51 @@ __device__ __forceinline__ void interval_block(const MaskArgs &m, int q0, int q1
   }
 }
 
+// DOCUMENT flags of key block [k0, k1] against query block [q0, q1], whose
+// ids are in qdoc with summary (qmin, qmax, q_uniform).  Blocks wholly above
+// the diagonal hold no visible pair; blocks that straddle it hold (i, i);
+// blocks wholly on or below it (k1 <= q0, every j <= i) are listed iff the
+// two blocks share an id and full iff one id covers both.
+__device__ __forceinline__ void document_block(const int32_t *doc_row, const int32_t *qdoc, int nq,
+                                               int qmin, int qmax, bool q_uniform, int q0, int q1,
+                                               int k0, int k1, bool &any, bool &all) {
+  any = false;
+  all = false;
+  if (k0 > q1) return;
+  if (k1 > q0) {
+    any = true;
+    return;
+  }
+  const int qval = qdoc[0];
+  int kmin = doc_row[k0], kmax = kmin;
+  bool k_uniform = true, hit_q = false;
+  for (int j = k0; j <= k1; ++j) {
+    const int d = doc_row[j];
+    kmin = min(kmin, d);
+    kmax = max(kmax, d);
+    k_uniform &= (d == kmin) && (d == kmax);
+    hit_q |= (d == qval);
+  }
+  if (kmax < qmin || kmin > qmax) return;
+  if (q_uniform) {
+    any = hit_q;
+    all = k_uniform && hit_q;
+    return;
+  }
+  if (k_uniform) {
+    for (int t = 0; t < nq && !any; ++t) any = (qdoc[t] == kmin);
+    return;
+  }
+  // General ids (not sorted, several per block): membership scan.
+  for (int j = k0; j <= k1 && !any; ++j) {
+    const int d = doc_row[j];
+    if (d < qmin || d > qmax) continue;
+    for (int t = 0; t < nq && !any; ++t) any = (qdoc[t] == d);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void block_mask_kernel(BMArgs a) {
   __shared__ int32_t qdoc[1024];
-  __shared__ int32_t kdoc[1024];
   __shared__ int32_t wave_cnt[kThreads / 64];
   __shared__ int32_t running;
 
@@ -70,51 +114,33 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(BMArgs a) {
   int32_t *idx_row = a.idx + row * a.nkb;
   uint8_t *full_row = a.full ? a.full + row * a.nkb : nullptr;
 
+  // Query-block ids and their summary (min, max, all equal).
+  int qmin = 0, qmax = 0;
+  bool q_uniform = true;
   if (doc) {
     for (int t = tid; t < nq; t += kThreads) qdoc[t] = doc_row[q0 + t];
+    __syncthreads();
+    qmin = qmax = qdoc[0];
+    for (int t = 0; t < nq; ++t) {
+      qmin = min(qmin, qdoc[t]);
+      qmax = max(qmax, qdoc[t]);
+    }
+    q_uniform = qmin == qmax;
   }
   if (tid == 0) running = 0;
   __syncthreads();
 
   for (int base = 0; base < a.nkb; base += kThreads) {
-    // Flags of key blocks base .. base + 255: one block per thread for the
-    // interval kinds; DOCUMENT scans each block with the whole workgroup.
+    // Flags of key blocks base .. base + 255, one block per thread.
     bool listed = false, full = false;
     const int kb = base + tid;
-    if (!doc) {
-      if (kb < a.nkb) {
-        const int k0 = kb * a.kv_block;
-        const int k1 = min(a.Skv, k0 + a.kv_block) - 1;
+    if (kb < a.nkb) {
+      const int k0 = kb * a.kv_block;
+      const int k1 = min(a.Skv, k0 + a.kv_block) - 1;
+      if (!doc)
         interval_block(a.mask, q0, q1, k0, k1, listed, full);
-      }
-    } else {
-      const int kend = min(a.nkb, base + kThreads);
-      for (int kk = base; kk < kend; ++kk) {
-        const int k0 = kk * a.kv_block;
-        const int k1 = min(a.Skv, k0 + a.kv_block) - 1;
-        const int nk = k1 - k0 + 1;
-        bool any_vis = false, all_vis = false;
-        if (k0 <= q1) {
-          __syncthreads();
-          for (int t = tid; t < nk; t += kThreads) kdoc[t] = doc_row[k0 + t];
-          __syncthreads();
-          int any_l = 0, all_l = 1;
-          const int pairs = nq * nk;
-          for (int pidx = tid; pidx < pairs; pidx += kThreads) {
-            const int ii = pidx / nk;
-            const int jj = pidx - ii * nk;
-            const bool v = (k0 + jj <= q0 + ii) && (kdoc[jj] == qdoc[ii]);
-            any_l |= v;
-            all_l &= v;
-          }
-          any_vis = __syncthreads_or(any_l) != 0;
-          all_vis = __syncthreads_and(all_l) != 0;
-        }
-        if (kk == kb) {
-          listed = any_vis;
-          full = all_vis;
-        }
-      }
+      else
+        document_block(doc_row, qdoc, nq, qmin, qmax, q_uniform, q0, q1, k0, k1, listed, full);
     }
 
     // Compact: rank of this thread's listed block among listed blocks.

@@ -30,7 +30,24 @@ BM_CASES = [
     ("prefix_lm", 1, 640, 640, 16, 1024, dict(prefix_len=0)),
     ("document", 2, 1000, 1000, 128, 128, dict(lengths=[300, 1, 129, 127, 443])),
     ("document", 1, 999, 999, 48, 80, dict(lengths=[10, 500, 489])),
+    # ids that are neither sorted nor contiguous: every decision path of the
+    # builder (summary tests, single-id blocks, the general scan)
+    ("document", 2, 700, 700, 64, 64, dict(random_ids=4)),
+    ("document", 1, 513, 513, 32, 128, dict(random_ids=40)),
+    ("document", 1, 600, 600, 128, 128, dict(pattern=[(0, 100), (1, 50), (0, 80), (2, 200), (1, 170)])),
+    ("document", 1, 257, 257, 128, 128, dict(lengths=[257])),     # one id; a 1-row last block
 ]
+
+
+def _case_doc_ids(B, S, kw):
+    if "lengths" in kw:
+        return _ids(kw["lengths"], B)
+    if "random_ids" in kw:
+        rng = np.random.default_rng(7)
+        return rng.integers(0, kw["random_ids"], size=(B, S)).astype(np.int32)
+    row = np.concatenate([np.full(n, d, np.int32) for d, n in kw["pattern"]])
+    assert row.size == S
+    return np.tile(row[None, :], (B, 1))
 
 
 @pytest.mark.parametrize("case", range(len(BM_CASES)))
@@ -39,7 +56,7 @@ def test_block_mask_bit_exact(case):
     dev = torch.device("cuda")
     doc = None
     if mask == "document":
-        doc = torch.from_numpy(_ids(kw["lengths"], B))
+        doc = torch.from_numpy(_case_doc_ids(B, Sq, kw))
     announce(f"block mask {BM_CASES[case][:6]}")
     bm = af.attn_build_block_mask(mask, B, Sq, Skv, q_block=qb, kv_block=kb,
                                   window=kw.get("window", 0), prefix_len=kw.get("prefix_len", 0),

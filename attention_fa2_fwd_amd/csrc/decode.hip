@@ -12,10 +12,13 @@
 //  * workgroup = (sequence, kv head, group of up to 4 query heads, split of
 //    64 pages = 1024 tokens); its 4 waves take the split's pages round-robin,
 //    so each K/V byte read serves every query head of the group (GQA);
-//  * a page of one kv head is one contiguous 4 KiB block of K (and of V);
-//    lane = 8 token slots x 8 slices of 16 d, so a wave reads a page's first
-//    8 tokens as 2 KiB of consecutive bytes, and the next page is loaded
-//    while the current one is reduced;
+//  * a page of one kv head is one contiguous 4 KiB block of K (and of V),
+//    read through a buffer resource of its own (an out-of-pool page id gets
+//    an empty range and reads as zeros); lane = 8 token slots x 2 chunks of
+//    8 d, so each load instruction reads whole 128-byte half rows; the
+//    split's page ids are read once up front and each page's id is taken
+//    into a scalar register, so the loop issues no dependent loads and the
+//    next page is in flight while the current one is reduced;
 //  * scores use v_dot2_f32_bf16 on the packed bf16 pairs, reduced over the 8
 //    slices with ds_swizzle; each lane keeps its own running max / sum / O
 //    (no cross-lane traffic per token), merged across lanes and waves once
@@ -32,6 +35,8 @@ constexpr int kSplitPages = 64;
 constexpr int kD = 128;
 constexpr int kPage = 16;
 constexpr float kRescaleThresh = 8.0f;   // log2 units: keep p <= 2^8 between rescales
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
+constexpr int kBufferFlags = 0x00020000;
 
 struct DecArgs {
   const __bf16 *q, *kc, *vc;
@@ -61,9 +66,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t8 = lane >> 3;        // token slot (tokens t8 and t8 + 8 of a page)
-  const int e8 = lane & 7;         // d slice [16 e8, 16 e8 + 16)
+  const int e8 = lane & 7;         // d chunks [8 e8, 8 e8 + 8) and [64 + 8 e8, 64 + 8 e8 + 8)
   const int split = blockIdx.x;
   const int hkv = blockIdx.y / a.n_hgroups;
   const int hg = blockIdx.y - hkv * a.n_hgroups;
@@ -78,12 +83,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
   const int p_end = min(n_pages, p_begin + kSplitPages);
   const int qpos = L - 1;
 
-  // This lane's slice of the GH queries, as packed bf16 pairs.
+  // Page ids of the split, one per lane (kSplitPages == 64), read once so the
+  // page loop issues no dependent loads: each page's id is taken with
+  // readlane into a scalar register.
+  static_assert(kSplitPages == 64, "one page id per lane");
+  const int32_t *ptab = a.page_table + (size_t)s * a.max_pages;
+  const int my_page = (p_begin + lane < p_end) ? ptab[p_begin + lane] : -1;
+
+  // This lane's slice of the GH queries, as packed bf16 pairs (the same two
+  // d chunks as its K/V loads).
   uint32_t qv[GH][8];
 #pragma unroll
   for (int g = 0; g < GH; ++g) {
-    const u32x4 *src = (const u32x4 *)(a.q + ((size_t)s * a.Hq + hq0 + g) * kD + 16 * e8);
-    const u32x4 w0 = src[0], w1 = src[1];
+    const __bf16 *src = a.q + ((size_t)s * a.Hq + hq0 + g) * kD;
+    const u32x4 w0 = *(const u32x4 *)(src + 8 * e8);
+    const u32x4 w1 = *(const u32x4 *)(src + 64 + 8 * e8);
     qv[g][0] = w0[0]; qv[g][1] = w0[1]; qv[g][2] = w0[2]; qv[g][3] = w0[3];
     qv[g][4] = w1[0]; qv[g][5] = w1[1]; qv[g][6] = w1[2]; qv[g][7] = w1[3];
   }
@@ -101,23 +115,30 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
     for (int d = 0; d < 16; ++d) o[g][d] = 0.0f;
   }
 
-  const int32_t *ptab = a.page_table + (size_t)s * a.max_pages;
-  const size_t head_stride = (size_t)kPage * kD;           // elements per (page, kv head)
-
-  // Page loads: K/V of tokens t8 and t8 + 8, d slice e8 (2 x 32 bytes each).
-  auto load_page = [&](int pi, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
-    int page = ptab[pi];
+  // One (page, kv head) block is 16 tokens x 256 bytes of K (and of V).  A
+  // buffer resource per block: an id outside the pool gets an empty range,
+  // so its loads return zeros without any wait or branch.
+  constexpr int kBlockBytes = kPage * kD * 2;
+  auto block_rsrc = [&](const __bf16 *cache, int page) {
     const bool ok = (page >= 0) && (page < a.num_pages);
-    page = ok ? page : 0;
-    const size_t base = ((size_t)page * a.Hkv + hkv) * head_stride + (size_t)t8 * kD + 16 * e8;
-    const u32x4 *kp = (const u32x4 *)(a.kc + base);
-    const u32x4 *vp = (const u32x4 *)(a.vc + base);
-    const int far = 8 * kD / 8;                       // 8 tokens ahead, in u32x4 units
-    kr[0] = kp[0]; kr[1] = kp[1]; kr[2] = kp[far]; kr[3] = kp[far + 1];
-    vr[0] = vp[0]; vr[1] = vp[1]; vr[2] = vp[far]; vr[3] = vp[far + 1];
-    if (!ok) {
+    const __bf16 *base = cache + ((size_t)(ok ? page : 0) * a.Hkv + hkv) * (kPage * kD);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, ok ? kBlockBytes : 0, kBufferFlags);
+  };
+  // Lane (t8, e8) loads 16 bytes at d 8 e8 and 16 at d 64 + 8 e8 of tokens
+  // t8 and t8 + 8: each load instruction reads 8 whole 128-byte half rows.
+  const int ld_off = t8 * (kD * 2) + e8 * 16;
+  // Loads are issued for every prefetch slot, past the split's end too (as
+  // an empty range), so the number of loads in flight is the same on every
+  // path and each wait covers only the page about to be reduced.
+  auto load_page = [&](int pi, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+    const int page = (pi < p_end) ? __builtin_amdgcn_readlane(my_page, min(pi - p_begin, 63)) : -1;
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc, page);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc, page);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { kr[i] = u32x4{0u, 0u, 0u, 0u}; vr[i] = kr[i]; }
+    for (int i = 0; i < 4; ++i) {
+      const int off = ld_off + (i & 1) * 128 + (i >> 1) * 8 * (kD * 2);
+      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
   };
 
@@ -177,17 +198,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
   // Pages of this split, round-robin over the waves, next page prefetched.
   int pi = p_begin + wave;
   u32x4 ka[4], va[4], kb[4], vb[4];
-  if (pi < p_end) load_page(pi, ka, va);
+  load_page(pi, ka, va);
   while (pi < p_end) {
-    const int pn = pi + 4;
-    if (pn < p_end) load_page(pn, kb, vb);
+    load_page(pi + 4, kb, vb);
     process_page(pi, ka, va);
-    pi = pn;
+    pi += 4;
     if (pi >= p_end) break;
-    const int pn2 = pi + 4;
-    if (pn2 < p_end) load_page(pn2, ka, va);
+    load_page(pi + 4, ka, va);
     process_page(pi, kb, vb);
-    pi = pn2;
+    pi += 4;
   }
 
   // Merge the 8 token slots of the wave (lanes e8, e8 + 8, ..., e8 + 56).
@@ -212,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
     }
     if (lane < 8) {
 #pragma unroll
-      for (int d = 0; d < 16; ++d) red_o[wave][g][16 * e8 + d] = o[g][d];
+      for (int d = 0; d < 16; ++d) red_o[wave][g][(d < 8 ? 0 : 56) + 8 * e8 + d] = o[g][d];
       if (lane == 0) {
         red_m[wave][g] = mm;
         red_l[wave][g] = lg;

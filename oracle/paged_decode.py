@@ -55,6 +55,12 @@ def paged_decode_ref(q, k_cache, v_cache, page_table, seq_lens, scale,
     lse = np.zeros((len(seqs), hq_count))
     for si, s in enumerate(seqs):
         length = int(np.asarray(seq_lens)[s])
+        if length <= 0:
+            # No key at all: the fully-masked-row convention, O = 0 and
+            # LSE = -inf.
+            out[si] = 0.0
+            lse[si] = -np.inf
+            continue
         kk, vv = gather_paged_kv(k_cache, v_cache, page_table, length, int(s))
         for hq in range(hq_count):
             hkv = _att.kv_head(hq, hq_count, hkv_count)

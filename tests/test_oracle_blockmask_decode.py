@@ -191,3 +191,16 @@ def test_split_combine_equals_unsplit():
             oc, lc = oracle.lse_combine_ref(op, lp)
             np.testing.assert_allclose(oc, o_full[0], atol=1e-14)
             assert lc == pytest.approx(l_full[0], abs=1e-13)
+
+
+def test_paged_decode_empty_sequence():
+    # A sequence with no token has no key to attend to: the fully masked row
+    # convention (O = 0, LSE = -inf), and the other sequences are unaffected.
+    q, kc, vc, table, lengths = _small_paged(seed=5)
+    lengths2 = np.array(lengths).copy()
+    lengths2[1] = 0
+    o1, l1 = oracle.paged_decode_ref(q, kc, vc, table, lengths, 0.3)
+    o2, l2 = oracle.paged_decode_ref(q, kc, vc, table, lengths2, 0.3)
+    assert np.all(o2[1] == 0.0) and np.all(l2[1] == -np.inf)
+    keep = [s for s in range(len(lengths)) if s != 1]
+    assert np.array_equal(o1[keep], o2[keep]) and np.array_equal(l1[keep], l2[keep])

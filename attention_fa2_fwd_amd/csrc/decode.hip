@@ -8,250 +8,283 @@
 // partial results: LSE = ln sum_k e^{lse_k}, O = sum_k e^{lse_k - LSE} O_k.
 //
 // The work is bound by HBM bandwidth (every valid K/V byte is read once per
-// kv head), so the design is about bytes in flight, not FLOPs:
-//  * workgroup = (sequence, kv head, group of up to 4 query heads, split of
-//    64 pages = 1024 tokens); its 4 waves take the split's pages round-robin,
-//    so each K/V byte read serves every query head of the group (GQA);
+// kv head), so the design keeps many bytes in flight and the arithmetic off
+// the critical path:
+//  * workgroup = (kv head, work item), the items being the 64-page (1024
+//    token) splits of every sequence in order; a workgroup finds its
+//    (sequence, split) from a prefix sum of the sequences' split counts, so
+//    the dispatch order holds every live item first and the workgroups past
+//    the last item (the grid is sized from max_pages_per_seq, as the host
+//    never reads the device-side lengths) come last and exit at once.  The
+//    4 waves take the split's pages round-robin.  All G <= 16 query heads of
+//    the kv head are processed together, so each K/V byte read serves every
+//    query head of the group (GQA);
+//  * the arithmetic is on the matrix cores: per page, S^T = K Q^T is four
+//    v_mfma_f32_16x16x32_bf16 (16 tokens x 16 head columns) and O^T += V^T P^T
+//    eight v_mfma_f32_16x16x16_bf16; the S^T accumulator is already the B
+//    operand of the second product, and V^T comes from ds_read_b64_tr_b16;
 //  * a page of one kv head is one contiguous 4 KiB block of K (and of V),
-//    read through a buffer resource of its own (an out-of-pool page id gets
-//    an empty range and reads as zeros); lane = 8 token slots x 2 chunks of
-//    8 d, so each load instruction reads whole 128-byte half rows; the
-//    split's page ids are read once up front and each page's id is taken
-//    into a scalar register, so the loop issues no dependent loads and the
-//    next page is in flight while the current one is reduced;
-//  * scores use v_dot2_f32_bf16 on the packed bf16 pairs, reduced over the 8
-//    slices with ds_swizzle; each lane keeps its own running max / sum / O
-//    (no cross-lane traffic per token), merged across lanes and waves once
-//    per split;
-//  * the grid is sized from max_pages_per_seq, so the host never reads the
-//    device-side lengths; splits past a sequence's end exit at once.
+//    read through a buffer resource of its own whose range ends at the
+//    sequence's last token: slots past it and out-of-pool page ids read as
+//    zeros, so they can never inject NaN through a zero weight.  K goes to
+//    registers (already in the MFMA A layout); V goes to LDS through
+//    buffer_load ... lds, three pages per wave in flight, into three LDS
+//    objects named at every access so that each read waits only for its
+//    own page;
+//  * the split's page ids are read once up front and each page's id is taken
+//    into a scalar register, so the page loop issues no dependent loads.
 #include "kernels.h"
 
 namespace attn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int kSplitPages = 64;
 constexpr int kD = 128;
 constexpr int kPage = 16;
-constexpr float kRescaleThresh = 8.0f;   // log2 units: keep p <= 2^8 between rescales
+constexpr int kRowBytes = kD * 2;
+constexpr int kBlockBytes = kPage * kRowBytes;   // one (page, kv head) block of K or V
+constexpr float kRescaleThresh = 8.0f;           // log2 units: keep p <= 2^8 between rescales
 // Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kBufferFlags = 0x00020000;
+// Cache policy bits of the K/V loads: the default (measured faster here than
+// the non-temporal hint, although every byte is read once).
+constexpr int kStreamAux = 0;
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct DecArgs {
   const __bf16 *q, *kc, *vc;
   const int32_t *page_table, *seq_lens;
-  int Hq, Hkv, max_pages, num_pages, n_hgroups, max_splits;
+  int n_seq, Hq, Hkv, max_pages, num_pages, max_splits;
   float scale_log2;
   ScoreArgs score;
   float *ws_o, *ws_lse;
 };
 
-__device__ __forceinline__ float swz_sum8(float v) {
-  // sum over the 8 lanes of an aligned 8-lane group (xor 1, 2, 4)
-  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x041F));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x081F));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x101F));
-  return v;
+__device__ __forceinline__ s16x4 lds_read_tr(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-
-template <int GH>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
-  __shared__ float red_o[4][GH][kD];
-  __shared__ float red_m[4][GH];
-  __shared__ float red_l[4][GH];
+  // V pages staged per wave: three slots, three separate LDS objects.
+  __shared__ __align__(16) char v_lds0[kWaves][kBlockBytes];
+  __shared__ __align__(16) char v_lds1[kWaves][kBlockBytes];
+  __shared__ __align__(16) char v_lds2[kWaves][kBlockBytes];
+  __shared__ float red_m[kWaves][16];
+  __shared__ float red_l[kWaves][16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t8 = lane >> 3;        // token slot (tokens t8 and t8 + 8 of a page)
-  const int e8 = lane & 7;         // d chunks [8 e8, 8 e8 + 8) and [64 + 8 e8, 64 + 8 e8 + 8)
-  const int split = blockIdx.x;
-  const int hkv = blockIdx.y / a.n_hgroups;
-  const int hg = blockIdx.y - hkv * a.n_hgroups;
-  const int s = blockIdx.z;
-  const int G = a.Hq / a.Hkv;
-  const int hq0 = hkv * G + hg * GH;
+  const int col = lane & 15;     // MFMA column: query head hq0 + col
+  const int grp = lane >> 4;     // 16-lane group
+  const int hkv = blockIdx.x % a.Hkv;
 
-  const int L = a.seq_lens[s];
+  // Work item blockIdx.x / Hkv: the items are the splits of sequence 0, then
+  // of sequence 1, ...  Find (s, split) from the inclusive prefix sum of the
+  // split counts, 64 sequences at a time.
+  int s = -1, split = 0;
+  {
+    int w = blockIdx.x / a.Hkv;
+    for (int c0 = 0; c0 < a.n_seq && s < 0; c0 += 64) {
+      const int i = c0 + lane;
+      int ns = 0;
+      if (i < a.n_seq) {
+        const int np = min(a.max_pages, (max(a.seq_lens[i], 0) + kPage - 1) / kPage);
+        ns = (np + kSplitPages - 1) / kSplitPages;
+      }
+      int incl = ns;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const unsigned long long hit = __ballot(incl > w);
+      if (hit) {
+        const int f = __builtin_ctzll(hit);
+        s = c0 + f;
+        split = w - (__shfl(incl, f) - __shfl(ns, f));
+      } else {
+        w -= __shfl(incl, 63);
+      }
+    }
+    s = __builtin_amdgcn_readfirstlane(s);
+    split = __builtin_amdgcn_readfirstlane(split);
+  }
+  if (s < 0) return;                                   // past the last item (uniform)
+  const int G = a.Hq / a.Hkv;
+  const int hq0 = hkv * G;
+
+  // The length is uniform; taken into a scalar register, everything derived
+  // from it (page range, buffer ranges) stays scalar.
+  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[s]);
   const int n_pages = min(a.max_pages, (max(L, 0) + kPage - 1) / kPage);
   const int p_begin = split * kSplitPages;
-  if (p_begin >= n_pages) return;                      // uniform across the workgroup
   const int p_end = min(n_pages, p_begin + kSplitPages);
   const int qpos = L - 1;
 
-  // Page ids of the split, one per lane (kSplitPages == 64), read once so the
-  // page loop issues no dependent loads: each page's id is taken with
-  // readlane into a scalar register.
-  static_assert(kSplitPages == 64, "one page id per lane");
+  // Page ids of the split, one per lane, read once.
+  static_assert(kSplitPages <= 64, "one page id per lane");
   const int32_t *ptab = a.page_table + (size_t)s * a.max_pages;
   const int my_page = (p_begin + lane < p_end) ? ptab[p_begin + lane] : -1;
 
-  // This lane's slice of the GH queries, as packed bf16 pairs (the same two
-  // d chunks as its K/V loads).
-  uint32_t qv[GH][8];
+  // Q^T fragments, the B operand of S^T = K Q^T: lane holds
+  // Q[hq0 + col][32c + 8 grp .. + 7]; columns past the group are zero.
+  bf16x8 qf[4];
 #pragma unroll
-  for (int g = 0; g < GH; ++g) {
-    const __bf16 *src = a.q + ((size_t)s * a.Hq + hq0 + g) * kD;
-    const u32x4 w0 = *(const u32x4 *)(src + 8 * e8);
-    const u32x4 w1 = *(const u32x4 *)(src + 64 + 8 * e8);
-    qv[g][0] = w0[0]; qv[g][1] = w0[1]; qv[g][2] = w0[2]; qv[g][3] = w0[3];
-    qv[g][4] = w1[0]; qv[g][5] = w1[1]; qv[g][6] = w1[2]; qv[g][7] = w1[3];
+  for (int c = 0; c < 4; ++c) {
+    qf[c] = bf16x8{};
+    if (col < G) qf[c] = *(const bf16x8 *)(a.q + ((size_t)s * a.Hq + hq0 + col) * kD + 32 * c + 8 * grp);
   }
-  float bias2[GH];
-#pragma unroll
-  for (int g = 0; g < GH; ++g) bias2[g] = bias_coeff(a.score, hq0 + g, a.Hq) * kLog2e;
+  const float bias2 = (col < G) ? bias_coeff(a.score, hq0 + col, a.Hq) * kLog2e : 0.0f;
   const bool has_bias = a.score.kind != ATTN_SCORE_NONE;
 
-  float m[GH], l[GH], o[GH][16];
+  // O^T accumulators: o[blk][i] = O[head col][d = 16 blk + 4 grp + i].
+  f32x4 o[8];
 #pragma unroll
-  for (int g = 0; g < GH; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int d = 0; d < 16; ++d) o[g][d] = 0.0f;
-  }
+  for (int b = 0; b < 8; ++b) o[b] = f32x4{};
+  float m_run = -INFINITY;   // reference max of column col (same in all 4 groups)
+  float l_run = 0.0f;        // this lane's share of the column's sum
 
-  // One (page, kv head) block is 16 tokens x 256 bytes of K (and of V).  A
-  // buffer resource per block: an id outside the pool gets an empty range,
-  // so its loads return zeros without any wait or branch.
-  constexpr int kBlockBytes = kPage * kD * 2;
-  auto block_rsrc = [&](const __bf16 *cache, int page) {
+  // Buffer resource of one (page, kv head) block, its range cut at the
+  // sequence's last token.
+  auto block_rsrc = [&](const __bf16 *cache, int page, int valid_bytes) __attribute__((always_inline)) {
     const bool ok = (page >= 0) && (page < a.num_pages);
     const __bf16 *base = cache + ((size_t)(ok ? page : 0) * a.Hkv + hkv) * (kPage * kD);
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, ok ? kBlockBytes : 0, kBufferFlags);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, ok ? valid_bytes : 0, kBufferFlags);
   };
-  // Lane (t8, e8) loads 16 bytes at d 8 e8 and 16 at d 64 + 8 e8 of tokens
-  // t8 and t8 + 8: each load instruction reads 8 whole 128-byte half rows.
-  const int ld_off = t8 * (kD * 2) + e8 * 16;
-  // Loads are issued for every prefetch slot, past the split's end too (as
-  // an empty range), so the number of loads in flight is the same on every
-  // path and each wait covers only the page about to be reduced.
-  auto load_page = [&](int pi, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+  // K fragment c of a page (A operand): lane holds K[token col][32c + 8 grp .. + 7].
+  const int k_off = col * kRowBytes + 16 * grp;
+  // V staging: load i writes rows 4i .. 4i + 3 of the block, lane L at byte
+  // 1024 i + 16 L (row 4i + L/16, slot L%16), taking the row's 16-byte chunk
+  // (L%16) ^ 2(L/16).  Row t of the staged block thus holds chunk c at slot
+  // c ^ 2(t%4), which spreads the transposed reads below over distinct banks.
+  const int v_off = (lane >> 4) * kRowBytes + 16 * ((lane & 15) ^ (2 * (lane >> 4)));
+  // Transposed V reads (A operand of O^T += V^T P^T, 16 d x 16 tokens): lane
+  // (grp, col) points at row t = 4 grp + col/4, d = 16 blk + 4 (col%4), i.e.
+  // chunk 2 blk + (col%4)/2 at slot 2 (blk ^ (col/4)) + (col%4)/2.  For
+  // blk = 4 b1 + b0 that is v_rd[b0] + 128 b1.
+  const int y = col >> 2;
+  int v_rd[4];
+#pragma unroll
+  for (int b0 = 0; b0 < 4; ++b0) v_rd[b0] = (4 * grp + y) * kRowBytes + 32 * (b0 ^ y) + 8 * (col & 3);
+
+  // Issue the loads of page pi: K fragments into kf, V into the LDS slot vt.
+  // Past the split's end the range is empty (the loads still issue, so the
+  // number in flight is the same on every path).
+  auto issue_page = [&](int pi, bf16x8 (&kf)[4], char *vt) __attribute__((always_inline)) {
     const int page = (pi < p_end) ? __builtin_amdgcn_readlane(my_page, min(pi - p_begin, 63)) : -1;
-    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc, page);
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc, page);
+    // Bytes of the block before the sequence's end (scalar: written with
+    // selects, not a min/max clamp that may be placed on the VALU).
+    const int rem = L - pi * kPage;
+    const int valid = rem >= kPage ? kBlockBytes : (rem > 0 ? rem * kRowBytes : 0);
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc, page, valid);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc, page, valid);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      kf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * c, 0, kStreamAux));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vt + 1024 * i), 16, v_off + 1024 * i, 0, 0,
+                                               kStreamAux);
+  };
+
+  // Online softmax and P.V of page pi.
+  auto process = [&](int pi, const bf16x8 (&kf)[4], const char *vt) __attribute__((always_inline)) {
+    f32x4 sacc = f32x4{};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[c], sacc, 0, 0, 0);
+    // sacc[i]: score of token 4 grp + i for head col.
+    const int j0 = pi * kPage + 4 * grp;
+    float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int off = ld_off + (i & 1) * 128 + (i >> 1) * 8 * (kD * 2);
-      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+      float v = sacc[i] * a.scale_log2;
+      if (has_bias) v = __builtin_fmaf(bias2, (float)(j0 + i - qpos), v);
+      x[i] = (j0 + i < L) ? v : -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // Raise the reference max only past the threshold.
+    const bool need = tmax > m_run + kRescaleThresh;
+    if (__any(need)) {
+      const float m_new = need ? tmax : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;   // 0 when m_run = -inf
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) o[b] *= alpha;
+    }
+    const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - mu);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    // P^T (B operand, 16 tokens x 16 heads): lane holds P[token 4 grp + j][col].
+    const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const s16x4 va = lds_read_tr(vt + v_rd[b & 3] + 128 * (b >> 2));
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[b], 0, 0, 0);
     }
   };
 
-  auto process_page = [&](int pi, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int j = pi * kPage + t8 + 8 * tt;
-      const bool valid = j < L;
-      float x[GH];
-#pragma unroll
-      for (int g = 0; g < GH; ++g) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t kw = kr[2 * tt + (u >> 2)][u & 3];
-          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv[g][u]),
-                                                __builtin_bit_cast(bf16x2, kw), acc, false);
-        }
-        acc = swz_sum8(acc);
-        float xx = acc * a.scale_log2;
-        if (has_bias) xx += bias2[g] * (float)(j - qpos);
-        x[g] = valid ? xx : -INFINITY;
-      }
-      // Rescale only when a score exceeds the running max by the threshold
-      // (the max is a stabiliser; the result does not depend on its value).
-#pragma unroll
-      for (int g = 0; g < GH; ++g) {
-        if (x[g] > m[g] + kRescaleThresh) {
-          const float alpha = fast_exp2(m[g] - x[g]);   // 0 when m = -inf
-          l[g] *= alpha;
-#pragma unroll
-          for (int d = 0; d < 16; ++d) o[g][d] *= alpha;
-          m[g] = x[g];
-        }
-      }
-      float vf[16];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t vw = vr[2 * tt + (u >> 2)][u & 3];
-        vf[2 * u] = bf_lo(vw);
-        vf[2 * u + 1] = bf_hi(vw);
-      }
-      // Tokens past the sequence end (tail of the last page) are skipped,
-      // not weighted by 0, so whatever those slots hold cannot leak in.
-      if (valid) {
-#pragma unroll
-        for (int g = 0; g < GH; ++g) {
-          const float p = fast_exp2(x[g] - m[g]);
-          l[g] += p;
-#pragma unroll
-          for (int d = 0; d < 16; ++d) o[g][d] = fmaf(p, vf[d], o[g][d]);
-        }
-      }
-    }
-  };
-
-  // Pages of this split, round-robin over the waves, next page prefetched.
+  // Pages of this split, round-robin over the waves, two pages ahead.
   int pi = p_begin + wave;
-  u32x4 ka[4], va[4], kb[4], vb[4];
-  load_page(pi, ka, va);
+  bf16x8 k0[4], k1[4], k2[4];
+  issue_page(pi, k0, v_lds0[wave]);
+  issue_page(pi + kWaves, k1, v_lds1[wave]);
   while (pi < p_end) {
-    load_page(pi + 4, kb, vb);
-    process_page(pi, ka, va);
-    pi += 4;
+    issue_page(pi + 2 * kWaves, k2, v_lds2[wave]);
+    process(pi, k0, v_lds0[wave]);
+    pi += kWaves;
     if (pi >= p_end) break;
-    load_page(pi + 4, ka, va);
-    process_page(pi, kb, vb);
-    pi += 4;
+    issue_page(pi + 2 * kWaves, k0, v_lds0[wave]);
+    process(pi, k1, v_lds1[wave]);
+    pi += kWaves;
+    if (pi >= p_end) break;
+    issue_page(pi + 2 * kWaves, k1, v_lds1[wave]);
+    process(pi, k2, v_lds2[wave]);
+    pi += kWaves;
   }
 
-  // Merge the 8 token slots of the wave (lanes e8, e8 + 8, ..., e8 + 56).
+  // Merge the waves.  Every staging load has landed before the V slots are
+  // reused for the partial O of each wave: [wave][head][d] as floats.
+  float lt = l_run + __shfl_xor(l_run, 16);
+  lt += __shfl_xor(lt, 32);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  static_assert(kWaves * 16 * kD * 4 <= 2 * kWaves * kBlockBytes, "partials fit in two V slots");
+  float *red_o0 = (float *)&v_lds0[0][0];   // waves 0, 1
+  float *red_o1 = (float *)&v_lds1[0][0];   // waves 2, 3
+  float *mine = (wave < 2 ? red_o0 : red_o1) + (wave & 1) * 16 * kD;
+  if (col < G) {
 #pragma unroll
-  for (int g = 0; g < GH; ++g) {
-    float mm = m[g];
-    mm = fmaxf(mm, __shfl_xor(mm, 8));
-    mm = fmaxf(mm, __shfl_xor(mm, 16));
-    mm = fmaxf(mm, __shfl_xor(mm, 32));
-    const float f = (m[g] == -INFINITY) ? 0.0f : fast_exp2(m[g] - mm);
-    float lg = l[g] * f;
-    lg += __shfl_xor(lg, 8);
-    lg += __shfl_xor(lg, 16);
-    lg += __shfl_xor(lg, 32);
-#pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      float v = o[g][d] * f;
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      o[g][d] = v;
-    }
-    if (lane < 8) {
-#pragma unroll
-      for (int d = 0; d < 16; ++d) red_o[wave][g][(d < 8 ? 0 : 56) + 8 * e8 + d] = o[g][d];
-      if (lane == 0) {
-        red_m[wave][g] = mm;
-        red_l[wave][g] = lg;
-      }
+    for (int b = 0; b < 8; ++b)
+      *(f32x4 *)(mine + col * kD + 16 * b + 4 * grp) = o[b];
+    if (grp == 0) {
+      red_m[wave][col] = m_run;
+      red_l[wave][col] = lt;
     }
   }
   __syncthreads();
 
-  // Merge the 4 waves; write the normalised partial and its natural-log LSE.
-  for (int idx = tid; idx < GH * kD; idx += kThreads) {
+  // Normalised partial and its natural-log LSE per (head, split).
+  for (int idx = tid; idx < G * kD; idx += kThreads) {
     const int g = idx / kD;
     const int d = idx - g * kD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][g]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][g]);
     float acc = 0.0f, tot = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float f = (red_m[w][g] == -INFINITY) ? 0.0f : fast_exp2(red_m[w][g] - M);
-      acc = fmaf(red_o[w][g][d], f, acc);
+      const float *ow = (w < 2 ? red_o0 : red_o1) + (w & 1) * 16 * kD;
+      acc = fmaf(ow[g * kD + d], f, acc);
       tot = fmaf(red_l[w][g], f, tot);
     }
     const size_t row = ((size_t)s * a.Hq + hq0 + g) * a.max_splits + split;
@@ -298,9 +331,8 @@ void decode_split_geometry(int max_pages, int *split_pages, int *max_splits) {
 }
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
-  const int G = p.Hq / p.Hkv;
-  const int GH = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   DecArgs a;
+  a.n_seq = p.N;
   a.q = (const __bf16 *)p.q;
   a.kc = (const __bf16 *)p.k_cache;
   a.vc = (const __bf16 *)p.v_cache;
@@ -310,16 +342,15 @@ hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
   a.Hkv = p.Hkv;
   a.max_pages = p.max_pages;
   a.num_pages = p.num_pages;
-  a.n_hgroups = G / GH;
   a.max_splits = p.max_splits;
   a.scale_log2 = p.scale * kLog2e;
   a.score = p.score;
   a.ws_o = p.ws_o;
   a.ws_lse = p.ws_lse;
-  const dim3 grid(p.max_splits, p.Hkv * a.n_hgroups, p.N);
-  if (GH == 4) hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(kThreads), 0, stream, a);
-  else if (GH == 2) hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kThreads), 0, stream, a);
-  else hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kThreads), 0, stream, a);
+  const size_t n_wg = (size_t)p.N * p.max_splits * p.Hkv;
+  if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n_wg);
+  hipLaunchKernelGGL(decode_split_kernel, grid, dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   CombArgs c;

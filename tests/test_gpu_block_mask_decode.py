@@ -147,6 +147,20 @@ def test_paged_decode_nan_poison_and_gqa_groups():
     run_decode(inp, "none", "poison G=1")
 
 
+def test_paged_decode_many_sequences_and_empty_ones():
+    # More sequences than one 64-wide chunk of the work enumeration, lengths
+    # that give 0, 1 and 2 splits, and empty sequences (O = 0, LSE = -inf).
+    rng = np.random.default_rng(11)
+    lengths = [int(x) for x in rng.integers(0, 200, size=150)]
+    lengths[0] = 0
+    lengths[70] = 0
+    lengths[149] = 0
+    lengths[5] = 1100
+    lengths[100] = 1024
+    inp = small_decode_inputs(lengths, hq=8, hkv=2, seed=4)
+    run_decode(inp, "alibi", "many sequences")
+
+
 def test_paged_decode_full_workload_sampled():
     w = workloads.PAGED_DECODE
     dev = torch.device("cuda")

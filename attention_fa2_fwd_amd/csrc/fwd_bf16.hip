@@ -40,7 +40,9 @@
 //    landing in another: each wave waits for its loads only at the barrier
 //    that ends the iteration.
 //  * exp2 with scale·log2(e) folded into one FMA; the running max is raised
-//    only when a tile exceeds it by a margin; LSE in natural log on output.
+//    only when a tile exceeds it by a margin; key tiles are visited last to
+//    first, so under causal-type masks and ALiBi the first tile already
+//    holds the row's largest scores; LSE in natural log on output.
 //  * Causal-type masks: workgroups with the most key tiles are launched
 //    first; waves skip tiles that hold no visible key for their rows and
 //    skip the predicate on tiles where every key is visible.
@@ -182,7 +184,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     t_first = lo / kBN;
     n_tiles = (hi > lo) ? (hi + kBN - 1) / kBN - t_first : 0;
   }
+  // Key tiles are visited from the last to the first: under causal-type
+  // masks the first one visited is the diagonal, and with a bias that grows
+  // with the key index (ALiBi) it carries the row's largest scores, so the
+  // running max is set early and rarely raised afterwards.
   auto tile_key0 = [&](int n) __attribute__((always_inline)) -> int {
+    n = n_tiles - 1 - n;
     if (bm_list) {
       const int bi = n / a.tiles_per_block;
       const int blk = s_blk[bi];   // bi < n_blocks <= kListCap
@@ -192,6 +199,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     return (t_first + n) * kBN;
   };
   auto tile_block_full = [&](int n) __attribute__((always_inline)) -> bool {
+    n = n_tiles - 1 - n;
     if (!bm_flags) return false;
     const int bi = n / a.tiles_per_block;
     return s_full[bi] != 0;

@@ -12,7 +12,12 @@ one taken here:
   page_table[s, t // page_size] at slot t % page_size; entries past
   ceil(L_s / page_size) are never read;
 * the single query of sequence s sits at position L_s - 1 and sees every key
-  t < L_s; score modifiers use i = L_s - 1.
+  t < L_s; score modifiers use i = L_s - 1;
+* with a sliding window (PagedAttention and the sliding window both stand in
+  the [FlexAttention page] variant list; the window is that of its §Sliding
+  Window + Causal, read as 0 <= i - t < W) the query sees only the keys with
+  L_s - W <= t < L_s; the cache slots of the other keys take no part, whatever
+  they hold.
 
 Split combine ([Online-Softmax page]: the online-softmax rescaling merges
 partial results): with per-range results (O_k normalised, lse_k),
@@ -24,7 +29,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import attention as _att
-from .attention import MaskSpec, ScoreSpec, MASK_NONE, attention_rows
+from .attention import MaskSpec, ScoreSpec, MASK_NONE, MASK_SLIDING, attention_rows
 
 
 def gather_paged_kv(k_cache, v_cache, page_table, seq_len: int, s: int):
@@ -41,12 +46,15 @@ def gather_paged_kv(k_cache, v_cache, page_table, seq_len: int, s: int):
 
 
 def paged_decode_ref(q, k_cache, v_cache, page_table, seq_lens, scale,
-                     score: ScoreSpec = ScoreSpec(), seqs=None):
+                     score: ScoreSpec = ScoreSpec(), seqs=None, mask: MaskSpec = MaskSpec(MASK_NONE)):
     """Decode attention of one query per sequence over its paged K/V.
 
-    q: [N, Hq, D].  Returns (O [N', Hq, D], LSE [N', Hq]) float64 for the
-    sequences in seqs (default all).
+    q: [N, Hq, D].  mask: MASK_NONE or MASK_SLIDING (window).  Returns
+    (O [N', Hq, D], LSE [N', Hq]) float64 for the sequences in seqs (default
+    all).
     """
+    if mask.kind not in (MASK_NONE, MASK_SLIDING):
+        raise ValueError("paged decode takes no mask or a sliding window")
     q = np.asarray(q)
     n_seq, hq_count, _ = q.shape
     hkv_count = np.asarray(k_cache).shape[1]
@@ -62,11 +70,16 @@ def paged_decode_ref(q, k_cache, v_cache, page_table, seq_lens, scale,
             lse[si] = -np.inf
             continue
         kk, vv = gather_paged_kv(k_cache, v_cache, page_table, length, int(s))
+        if mask.kind == MASK_SLIDING:
+            # keys before the window are masked below; their slots' contents
+            # take no part (zeroed, so that no stored value can leak in)
+            t0 = max(0, length - mask.window)
+            kk[:, :t0] = 0.0
+            vv[:, :t0] = 0.0
         for hq in range(hq_count):
             hkv = _att.kv_head(hq, hq_count, hkv_count)
             o, l = attention_rows(q[s, hq][None, :].astype(np.float64), kk[hkv], vv[hkv],
-                                  [length - 1], int(s), hq, hq_count, scale,
-                                  MaskSpec(MASK_NONE), score)
+                                  [length - 1], int(s), hq, hq_count, scale, mask, score)
             out[si, hq] = o[0]
             lse[si, hq] = l[0]
     return out, lse

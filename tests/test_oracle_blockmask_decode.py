@@ -204,3 +204,54 @@ def test_paged_decode_empty_sequence():
     assert np.all(o2[1] == 0.0) and np.all(l2[1] == -np.inf)
     keep = [s for s in range(len(lengths)) if s != 1]
     assert np.array_equal(o1[keep], o2[keep]) and np.array_equal(l1[keep], l2[keep])
+
+
+@pytest.mark.parametrize("window", [1, 3, 4, 5, 17, 1000])
+def test_paged_decode_sliding_window(window):
+    # Windowed decode equals contiguous attention of the query row L-1 under
+    # the sliding-window mask, computed token by token.
+    q, kc, vc, table, lengths = _small_paged(seed=6)
+    n, hq, d = q.shape
+    hkv, page = kc.shape[1], kc.shape[2]
+    ms = MaskSpec(MASK_SLIDING, window=window)
+    score = ScoreSpec(SCORE_ALIBI)
+    o, lse = oracle.paged_decode_ref(q, kc, vc, table, lengths, 0.25, score, mask=ms)
+    for s in range(n):
+        L = int(lengths[s])
+        kk = np.zeros((1, hkv, L, d))
+        vv = np.zeros((1, hkv, L, d))
+        for t in range(L):
+            p = table[s, t // page]
+            kk[0, :, t] = kc[p, :, t % page]
+            vv[0, :, t] = vc[p, :, t % page]
+        qq = np.zeros((1, hq, L, d))
+        qq[0, :, L - 1] = q[s]
+        oc, lc = oracle.attention_ref(qq, kk, vv, 0.25, ms, score, rows=[L - 1])
+        np.testing.assert_allclose(o[s], oc[0, :, 0], atol=1e-13)
+        np.testing.assert_allclose(lse[s], lc[0, :, 0], atol=1e-13)
+
+
+def test_paged_decode_window_closed_forms():
+    q, kc, vc, table, lengths = _small_paged(seed=7)
+    page = kc.shape[2]
+    # window 1: the query sees only its own key, O = V[L-1], LSE = its score
+    o1, l1 = oracle.paged_decode_ref(q, kc, vc, table, lengths, 0.3, mask=MaskSpec(MASK_SLIDING, window=1))
+    for s, L in enumerate(lengths):
+        p = table[s, (int(L) - 1) // page]
+        np.testing.assert_allclose(o1[s], vc[p, :, (int(L) - 1) % page].repeat(4, axis=0), atol=1e-13)
+        kv = kc[p, :, (int(L) - 1) % page].repeat(4, axis=0)
+        np.testing.assert_allclose(l1[s], 0.3 * np.sum(q[s] * kv, axis=-1), atol=1e-12)
+    # a window at least as long as every sequence: no window
+    o2, l2 = oracle.paged_decode_ref(q, kc, vc, table, lengths, 0.3,
+                                     mask=MaskSpec(MASK_SLIDING, window=int(max(lengths))))
+    o3, l3 = oracle.paged_decode_ref(q, kc, vc, table, lengths, 0.3)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
+    # slots before the window take no part, whatever they hold
+    kc2, vc2 = kc.copy(), vc.copy()
+    for s, L in enumerate(lengths):
+        for t in range(max(0, int(L) - 3)):
+            kc2[table[s, t // page], :, t % page] = np.nan
+            vc2[table[s, t // page], :, t % page] = np.nan
+    o4, l4 = oracle.paged_decode_ref(q, kc2, vc2, table, lengths, 0.3, mask=MaskSpec(MASK_SLIDING, window=3))
+    o5, l5 = oracle.paged_decode_ref(q, kc, vc, table, lengths, 0.3, mask=MaskSpec(MASK_SLIDING, window=3))
+    assert np.array_equal(o4, o5) and np.array_equal(l4, l5)

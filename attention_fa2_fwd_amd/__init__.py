@@ -92,8 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_paged_decode_workspace_size.restype = ctypes.c_size_t
     lib.attn_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                      i32, i32, f32, i32, ctypes.POINTER(ScoreParams), vp,
-                                      ctypes.c_size_t, vp]
+                                      i32, i32, f32, i32, ctypes.POINTER(MaskParams), i32,
+                                      ctypes.POINTER(ScoreParams), vp, ctypes.c_size_t, vp]
     lib.attn_paged_decode.restype = i32
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
@@ -196,10 +196,12 @@ def attn_paged_decode_workspace_size(num_seqs: int, Hq: int, D: int, max_pages_p
 
 
 def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optional[float] = None,
-                      score: str = "none", alibi_slopes=None, rel_scale: float = 1.0,
-                      workspace=None, out=None, lse=None):
+                      mask: str = "none", window: int = 0, score: str = "none", alibi_slopes=None,
+                      rel_scale: float = 1.0, workspace=None, out=None, lse=None):
     """Paged split-KV decode.  q [N,Hq,D] bf16; caches [pages,Hkv,page,D] bf16;
-    page_table int32 [N,max_pages]; seq_lens int32 [N].  Returns (out, lse)."""
+    page_table int32 [N,max_pages]; seq_lens int32 [N]; mask "none" or
+    "sliding" (the query at seq_lens-1 sees the last `window` keys).
+    Returns (out, lse)."""
     lib = load_library()
     n, hq, d = q.shape
     pages, hkv, page_size, _ = k_cache.shape
@@ -219,10 +221,14 @@ def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optio
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     sk, sp = _score_params(score, alibi_slopes, rel_scale)
+    if mask not in MASK_KINDS:
+        raise ValueError(f"unknown mask {mask!r}")
+    mp = MaskParams(int(window), 0, None)
     rc = lib.attn_paged_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                page_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                                lse.data_ptr(), BF16, n, hq, hkv, d, page_size, max_pages, pages,
-                               float(scale), sk, ctypes.byref(sp), workspace.data_ptr(),
+                               float(scale), MASK_KINDS[mask], ctypes.byref(mp), sk,
+                               ctypes.byref(sp), workspace.data_ptr(),
                                workspace.numel() * workspace.element_size(), _stream(q.device))
     _check("attn_paged_decode", rc)
     return out, lse

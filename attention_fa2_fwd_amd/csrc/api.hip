@@ -182,7 +182,8 @@ size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int D, int max_pag
 int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *page_table, const int32_t *seq_lens, void *out, float *lse,
                       attn_dtype_t dt, int N, int Hq, int Hkv, int D, int page_size,
-                      int max_pages_per_seq, int num_pages, float scale, attn_score_kind_t sk,
+                      int max_pages_per_seq, int num_pages, float scale, attn_mask_kind_t mk,
+                      const attn_mask_params_t *mp, attn_score_kind_t sk,
                       const attn_score_params_t *sp, void *workspace, size_t workspace_bytes,
                       void *stream) {
   if (N < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
@@ -195,7 +196,12 @@ int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
   if (page_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports page_size == 16");
   if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports Hq/Hkv <= 16");
   attn::DecodeParams p{};
-  int rc = check_score(sk, sp, &p.score);
+  if (!valid_mask_kind(mk)) return fail(ATTN_ERR_INVALID, "unknown mask kind %d", mk);
+  if (mk != ATTN_MASK_NONE && mk != ATTN_MASK_SLIDING)
+    return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports mask kinds NONE and SLIDING");
+  int rc = check_mask(mk, mp, 1, 1, &p.mask);
+  if (rc) return rc;
+  rc = check_score(sk, sp, &p.score);
   if (rc) return rc;
   if (N == 0) {
     g_err[0] = '\0';

@@ -54,10 +54,20 @@ constexpr int kStreamAux = 0;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Keys a decode query sees: t in [t0, L) with t0 = max(0, L - window) under a
+// sliding window (window = 0: no window), held in pages [pf, pe).
+__device__ __forceinline__ void key_range(int L, int window, int max_pages, int &t0, int &pf, int &pe) {
+  L = max(L, 0);
+  pe = min(max_pages, (L + kPage - 1) / kPage);
+  t0 = window > 0 ? max(0, L - window) : 0;
+  pf = min(t0 / kPage, pe);
+}
+
 struct DecArgs {
   const __bf16 *q, *kc, *vc;
   const int32_t *page_table, *seq_lens;
   int n_seq, Hq, Hkv, max_pages, num_pages, max_splits;
+  int window;      // sliding window of the decode query, 0 = none
   float scale_log2;
   ScoreArgs score;
   float *ws_o, *ws_lse;
@@ -92,8 +102,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
       const int i = c0 + lane;
       int ns = 0;
       if (i < a.n_seq) {
-        const int np = min(a.max_pages, (max(a.seq_lens[i], 0) + kPage - 1) / kPage);
-        ns = (np + kSplitPages - 1) / kSplitPages;
+        int t0, pf, pe;
+        key_range(a.seq_lens[i], a.window, a.max_pages, t0, pf, pe);
+        ns = (pe - pf + kSplitPages - 1) / kSplitPages;
       }
       int incl = ns;
 #pragma unroll
@@ -120,9 +131,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
   // The length is uniform; taken into a scalar register, everything derived
   // from it (page range, buffer ranges) stays scalar.
   const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[s]);
-  const int n_pages = min(a.max_pages, (max(L, 0) + kPage - 1) / kPage);
-  const int p_begin = split * kSplitPages;
-  const int p_end = min(n_pages, p_begin + kSplitPages);
+  int t0, p_first, p_stop;
+  key_range(L, a.window, a.max_pages, t0, p_first, p_stop);
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  const int p_begin = __builtin_amdgcn_readfirstlane(p_first + split * kSplitPages);
+  const int p_end = __builtin_amdgcn_readfirstlane(min(p_stop, p_begin + kSplitPages));
   const int qpos = L - 1;
 
   // Page ids of the split, one per lane, read once.
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
     for (int i = 0; i < 4; ++i) {
       float v = sacc[i] * a.scale_log2;
       if (has_bias) v = __builtin_fmaf(bias2, (float)(j0 + i - qpos), v);
-      x[i] = (j0 + i < L) ? v : -INFINITY;
+      x[i] = (j0 + i < L && j0 + i >= t0) ? v : -INFINITY;
     }
     float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
@@ -225,10 +238,27 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
     l_run += (p[0] + p[1]) + (p[2] + p[3]);
     // P^T (B operand, 16 tokens x 16 heads): lane holds P[token 4 grp + j][col].
     const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+    // The V^T fragment of a lane covers the same tokens 4 grp + j as its P^T
+    // fragment.  In the page that holds the window's first key, the rows of
+    // the keys before it are cleared: their p is 0, but 0 times a NaN left in
+    // the cache is not 0.  The test is uniform, so other pages skip it.
+    if (pi * kPage < t0) {
+      uint64_t keep = ~0ull;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const s16x4 va = lds_read_tr(vt + v_rd[b & 3] + 128 * (b >> 2));
-      o[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[b], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        if (j0 + j < t0) keep &= ~(0xffffull << (16 * j));
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint64_t raw = __builtin_bit_cast(uint64_t, lds_read_tr(vt + v_rd[b & 3] + 128 * (b >> 2)));
+        const s16x4 va = __builtin_bit_cast(s16x4, raw & keep);
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[b], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const s16x4 va = lds_read_tr(vt + v_rd[b & 3] + 128 * (b >> 2));
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[b], 0, 0, 0);
+      }
     }
   };
 
@@ -295,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
 
 struct CombArgs {
   const int32_t *seq_lens;
-  int Hq, max_pages, max_splits;
+  int Hq, max_pages, max_splits, window;
   const float *ws_o, *ws_lse;
   __bf16 *out;
   float *lse;
@@ -306,9 +336,9 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(CombArgs a) {
   const int hq = blockIdx.x;
   const int s = blockIdx.y;
   const int d = threadIdx.x;
-  const int L = a.seq_lens[s];
-  const int n_pages = min(a.max_pages, (max(L, 0) + kPage - 1) / kPage);
-  const int ns = (n_pages + kSplitPages - 1) / kSplitPages;
+  int t0, pf, pe;
+  key_range(a.seq_lens[s], a.window, a.max_pages, t0, pf, pe);
+  const int ns = (pe - pf + kSplitPages - 1) / kSplitPages;
   const size_t row0 = ((size_t)s * a.Hq + hq) * a.max_splits;
   float M = -INFINITY;
   for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ws_lse[row0 + k]);
@@ -333,6 +363,7 @@ void decode_split_geometry(int max_pages, int *split_pages, int *max_splits) {
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
   DecArgs a;
   a.n_seq = p.N;
+  a.window = (p.mask.kind == ATTN_MASK_SLIDING) ? p.mask.window : 0;
   a.q = (const __bf16 *)p.q;
   a.kc = (const __bf16 *)p.k_cache;
   a.vc = (const __bf16 *)p.v_cache;
@@ -358,6 +389,7 @@ hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
   c.Hq = p.Hq;
   c.max_pages = p.max_pages;
   c.max_splits = p.max_splits;
+  c.window = a.window;
   c.ws_o = p.ws_o;
   c.ws_lse = p.ws_lse;
   c.out = (__bf16 *)p.out;

@@ -43,6 +43,7 @@ struct DecodeParams {
   float *lse;
   int N, Hq, Hkv, D, page_size, max_pages, num_pages;
   float scale;
+  MaskArgs mask;   // NONE or SLIDING
   ScoreArgs score;
   float *ws_o;     // [N, Hq, max_splits, D]
   float *ws_lse;   // [N, Hq, max_splits]

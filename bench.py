@@ -121,7 +121,9 @@ def bench_prefill(af, torch, workloads, w, steps, warmup, out_dtype=None, with_b
     return res
 
 
-def bench_decode(af, torch, workloads, steps, warmup):
+def bench_decode(af, torch, workloads, steps, warmup, window=0, score="none"):
+    """Paged decode of the 64-sequence workload; with window > 0 each query
+    sees its last `window` keys (and only those are counted as read)."""
     dev = torch.device("cuda")
     w = workloads.PAGED_DECODE
     inp = workloads.decode_inputs(w, device=dev)
@@ -131,7 +133,8 @@ def bench_decode(af, torch, workloads, steps, warmup):
     out = torch.empty_like(inp["q"])
     lse = torch.empty((n, hq), dtype=torch.float32, device=dev)
     args = (inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"], inp["seq_lens"])
-    kw = dict(scale=1.0 / math.sqrt(d), workspace=ws, out=out, lse=lse)
+    kw = dict(scale=1.0 / math.sqrt(d), workspace=ws, out=out, lse=lse,
+              mask="sliding" if window else "none", window=window, score=score)
     for _ in range(warmup):
         af.attn_paged_decode(*args, **kw)
     torch.cuda.synchronize()
@@ -142,13 +145,15 @@ def bench_decode(af, torch, workloads, steps, warmup):
     e1 = t.event()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    lengths = inp["lengths"]
-    kv_bytes = int(lengths.sum()) * 2 * w.Hkv * w.D * 2
-    pages = int(sum(-(-int(L) // w.page_size) for L in lengths))
+    lengths = [int(L) for L in inp["lengths"]]
+    first = [max(0, L - window) if window else 0 for L in lengths]
+    tokens = sum(L - t0 for L, t0 in zip(lengths, first))
+    kv_bytes = tokens * 2 * w.Hkv * w.D * 2
+    pages = sum(-(-L // w.page_size) - t0 // w.page_size for L, t0 in zip(lengths, first))
     algo_bytes = kv_bytes + n * hq * d * 2 * 2 + n * hq * 4 + pages * 4 + n * 4
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     return {"ms": ms, "GB_per_s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
-            "algorithmic_bytes": algo_bytes, "tokens": int(lengths.sum())}
+            "algorithmic_bytes": algo_bytes, "tokens": tokens}
 
 
 def cpu_baseline(workloads, budget_s: float = 12.0):
@@ -191,7 +196,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="run one workload (dense, causal, gqa, document, decode) and exit")
+                    help="run one workload (dense, causal, gqa, document, decode, decode_window) and exit")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy, to calibrate byte counters")
     args = ap.parse_args()
@@ -226,6 +231,8 @@ def main():
                "gqa": workloads.GQA_WINDOW_ALIBI, "document": workloads.DOCUMENT_BLOCKMASK}
         if args.only == "decode":
             r = bench_decode(af, torch, workloads, args.steps, args.warmup)
+        elif args.only == "decode_window":
+            r = bench_decode(af, torch, workloads, args.steps, args.warmup, window=1024, score="alibi")
         else:
             r = bench_prefill(af, torch, workloads, sel[args.only], args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **r}), flush=True)
@@ -317,6 +324,9 @@ def main():
             extra[name] = bench_prefill(af, torch, workloads, w, 20, 3)
         print("[bench] paged decode", file=sys.stderr, flush=True)
         extra["paged_decode"] = bench_decode(af, torch, workloads, 20, 3)
+        print("[bench] paged decode, window 1024 + alibi", file=sys.stderr, flush=True)
+        extra["paged_decode_window1024_alibi"] = bench_decode(af, torch, workloads, 20, 3,
+                                                              window=1024, score="alibi")
         line["workloads"] = {k2: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                                   for kk, vv in r.items()} for k2, r in extra.items()}
         line["workloads"]["dense_causal_split"] = {

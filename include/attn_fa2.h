@@ -164,18 +164,25 @@ size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int D, int max_pag
  *   page_table int32 [N, max_pages_per_seq]; token t of sequence s sits in
  *              page page_table[s, t / page_size], slot t % page_size;
  *              entries past ceil(seq_lens[s] / page_size) are never read
- *   seq_lens   int32 [N], each in [1, max_pages_per_seq * page_size]
+ *   seq_lens   int32 [N], each in [0, max_pages_per_seq * page_size]; a
+ *              sequence of length 0 gets O = 0 and LSE = -inf
  *   out        [N, Hq, D] bf16 (written); lse [N, Hq] float32 (written)
- *   The query of sequence s sits at position seq_lens[s] - 1 and sees every
- *   key t < seq_lens[s]; ALIBI / REL_POS use i = seq_lens[s] - 1.
+ *   The query of sequence s sits at position i = seq_lens[s] - 1.  With
+ *   mk = ATTN_MASK_NONE it sees every key t <= i; with ATTN_MASK_SLIDING
+ *   (PagedAttention + sliding window, both in the FlexAttention write-up's
+ *   variant list; window as in its §Sliding Window + Causal) it sees the
+ *   keys with 0 <= i - t < mp->window: pages wholly before the window are
+ *   never read, and what the slots of earlier keys hold (NaN included) has
+ *   no effect.  ALIBI / REL_POS use i = seq_lens[s] - 1.
  *   workspace: device scratch of at least
  *   attn_paged_decode_workspace_size(...) bytes, 256-byte aligned.
  * Supported: dt = BF16, D == 128, page_size == 16, Hq % Hkv == 0,
- * Hq / Hkv <= 16.                                                          */
+ * Hq / Hkv <= 16, mk in {NONE, SLIDING} (others return -2).               */
 int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *page_table, const int32_t *seq_lens, void *out, float *lse,
                       attn_dtype_t dt, int N, int Hq, int Hkv, int D, int page_size,
-                      int max_pages_per_seq, int num_pages, float scale, attn_score_kind_t sk,
+                      int max_pages_per_seq, int num_pages, float scale, attn_mask_kind_t mk,
+                      const attn_mask_params_t *mp, attn_score_kind_t sk,
                       const attn_score_params_t *sp, void *workspace, size_t workspace_bytes,
                       void *stream);
 

@@ -100,10 +100,13 @@ def test_block_mask_builder_checks():
     assert lib.attn_build_block_mask(1, ctypes.byref(mp), 0, 256, 256, 128, 128, None, None, None, None) == 0
 
 
-def _dec(lib, N=2, Hq=8, Hkv=2, D=128, page=16, max_pages=4, pool=8, dt=1, sk=0, ws=None, ws_bytes=0):
+def _dec(lib, N=2, Hq=8, Hkv=2, D=128, page=16, max_pages=4, pool=8, dt=1, mk=0, window=0, sk=0,
+         ws=None, ws_bytes=0):
+    mp = af.MaskParams(window, 0, None)
     sp = af.ScoreParams(None, 1.0)
     return lib.attn_paged_decode(None, None, None, None, None, None, None, dt, N, Hq, Hkv, D, page,
-                                 max_pages, pool, 0.1, sk, ctypes.byref(sp), ws, ws_bytes, None)
+                                 max_pages, pool, 0.1, mk, ctypes.byref(mp), sk, ctypes.byref(sp), ws,
+                                 ws_bytes, None)
 
 
 def test_paged_decode_checks():
@@ -113,6 +116,10 @@ def test_paged_decode_checks():
     assert _dec(lib, page=32) == -2
     assert _dec(lib, dt=0) == -2
     assert _dec(lib, Hq=34, Hkv=2) == -2
+    assert _dec(lib, mk=1) == -2                           # only NONE and SLIDING
+    assert _dec(lib, mk=9) == -1
+    assert _dec(lib, mk=2, window=0) == -1                 # window must be >= 1
+    assert _dec(lib, mk=2, window=100) == -1               # valid mask, null tensors
     assert _dec(lib, N=0) == 0
     assert _dec(lib) == -1                                 # null tensors
     need = lib.attn_paged_decode_workspace_size(2, 8, 128, 4, 16)

@@ -111,19 +111,22 @@ def small_decode_inputs(lengths, hq=8, hkv=2, max_pages=80, seed=0, poison=False
     return inp
 
 
-def run_decode(inp, score="none", label="", seqs=None):
+def run_decode(inp, score="none", label="", seqs=None, window=0):
     dev = torch.device("cuda")
     q = inp["q"]
     scale = 1.0 / math.sqrt(q.shape[-1])
-    announce(f"paged decode {label} {score}")
+    mask = "sliding" if window else "none"
+    announce(f"paged decode {label} {score} window={window}")
     out, lse = af.attn_paged_decode(q.to(dev), inp["k_cache"].to(dev), inp["v_cache"].to(dev),
                                     inp["page_table"].to(dev), inp["seq_lens"].to(dev),
-                                    scale=scale, score=score, rel_scale=-0.01)
+                                    scale=scale, mask=mask, window=window, score=score,
+                                    rel_scale=-0.01)
     torch.cuda.synchronize()
     ss = oracle.ScoreSpec(workloads.SCORE_NAMES[score], rel_scale=-0.01)
+    ms = oracle.MaskSpec(workloads.MASK_NAMES[mask], window=window)
     o_ref, l_ref = oracle.paged_decode_ref(f64(q), f64(inp["k_cache"]), f64(inp["v_cache"]),
                                            inp["page_table"].numpy(), inp["seq_lens"].numpy(),
-                                           scale, ss, seqs=seqs)
+                                           scale, ss, seqs=seqs, mask=ms)
     o = f64(out)
     l = f64(lse)
     if seqs is not None:
@@ -145,6 +148,27 @@ def test_paged_decode_nan_poison_and_gqa_groups():
     run_decode(inp, "alibi", "poison G=6")
     inp = small_decode_inputs([5, 64, 300], hq=3, hkv=3, seed=3, poison=True)
     run_decode(inp, "none", "poison G=1")
+
+
+@pytest.mark.parametrize("window", [1, 15, 16, 17, 100, 700, 5000])
+def test_paged_decode_sliding_window(window):
+    run_decode(small_decode_inputs(LENGTHS, seed=5), "alibi", "window", window=window)
+
+
+def test_paged_decode_window_skips_pages_before_it():
+    # NaN in every slot before each sequence's window: pages wholly before the
+    # window are never read, and the keys of the first page that precede the
+    # window get no weight.
+    lengths = [40, 300, 1100, 1280]
+    window = 37
+    inp = small_decode_inputs(lengths, hq=8, hkv=2, seed=6, poison=True)
+    table = inp["page_table"].numpy()
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16)
+    for s, L in enumerate(lengths):
+        for t in range(max(0, L - window)):
+            inp["k_cache"][table[s, t // 16], :, t % 16] = nan
+            inp["v_cache"][table[s, t // 16], :, t % 16] = nan
+    run_decode(inp, "none", "window poison", window=window)
 
 
 def test_paged_decode_many_sequences_and_empty_ones():
@@ -191,3 +215,37 @@ def test_paged_decode_full_workload_sampled():
                                          np.array([L], dtype=np.int32), scale)
         o_ref[i], l_ref[i] = o1[0], l1[0]
     compare(f64(out)[seqs], f64(lse)[seqs], o_ref, l_ref, torch.bfloat16, "paged decode full")
+
+
+def test_paged_decode_full_workload_window_alibi_sampled():
+    # The 64-sequence workload with a 1024-token window and ALiBi (the
+    # PagedAttention + sliding window combination), sampled sequences.
+    w = workloads.PAGED_DECODE
+    dev = torch.device("cuda")
+    announce("paged decode full workload window+alibi: generating")
+    inp = workloads.decode_inputs(w, device=dev)
+    lengths = inp["lengths"]
+    scale = 1.0 / math.sqrt(w.D)
+    announce("paged decode full workload window+alibi: run")
+    out, lse = af.attn_paged_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
+                                    inp["seq_lens"], scale=scale, mask="sliding", window=1024,
+                                    score="alibi")
+    torch.cuda.synchronize()
+    seqs = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), 0, 17, 63})
+    table = inp["page_table"].cpu().numpy()
+    q = inp["q"].cpu()
+    o_ref = np.zeros((len(seqs), w.Hq, w.D))
+    l_ref = np.zeros((len(seqs), w.Hq))
+    for i, s in enumerate(seqs):
+        L = int(lengths[s])
+        pages = table[s, :(L + 15) // 16]
+        pid = torch.from_numpy(pages.astype(np.int64)).to(dev)
+        kc = inp["k_cache"].index_select(0, pid).cpu()
+        vc = inp["v_cache"].index_select(0, pid).cpu()
+        local = np.arange(len(pages), dtype=np.int32)[None, :]
+        o1, l1 = oracle.paged_decode_ref(f64(q[s:s + 1]), f64(kc), f64(vc), local,
+                                         np.array([L], dtype=np.int32), scale,
+                                         oracle.ScoreSpec(oracle.SCORE_ALIBI),
+                                         mask=oracle.MaskSpec(oracle.MASK_SLIDING, window=1024))
+        o_ref[i], l_ref[i] = o1[0], l1[0]
+    compare(f64(out)[seqs], f64(lse)[seqs], o_ref, l_ref, torch.bfloat16, "paged decode full window")

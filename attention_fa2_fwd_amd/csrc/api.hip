@@ -172,9 +172,7 @@ size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int D, int max_pag
                                         int page_size) {
   (void)page_size;
   if (num_seqs <= 0 || Hq <= 0 || D <= 0 || max_pages_per_seq <= 0) return 0;
-  int split_pages = 0, max_splits = 0;
-  attn::decode_split_geometry(max_pages_per_seq, &split_pages, &max_splits);
-  const size_t rows = (size_t)num_seqs * Hq * max_splits;
+  const size_t rows = (size_t)num_seqs * Hq * attn::decode_max_splits(max_pages_per_seq);
   const size_t o_bytes = (rows * D * sizeof(float) + 255) / 256 * 256;
   return o_bytes + rows * sizeof(float);
 }
@@ -213,8 +211,7 @@ int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   if (((uintptr_t)workspace) % 256 != 0) return fail(ATTN_ERR_INVALID, "workspace must be 256-byte aligned");
-  int split_pages = 0, max_splits = 0;
-  attn::decode_split_geometry(max_pages_per_seq, &split_pages, &max_splits);
+  const int max_splits = attn::decode_max_splits(max_pages_per_seq);
   const size_t rows = (size_t)N * Hq * max_splits;
   p.q = q;
   p.k_cache = k_cache;
@@ -234,7 +231,6 @@ int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
   p.ws_o = (float *)workspace;
   p.ws_lse = (float *)((char *)workspace + (rows * D * sizeof(float) + 255) / 256 * 256);
   p.max_splits = max_splits;
-  p.split_pages = split_pages;
   return launch_result(attn::launch_paged_decode(p, (hipStream_t)stream), "attn_paged_decode");
 }
 

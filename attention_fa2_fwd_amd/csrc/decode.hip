@@ -10,12 +10,15 @@
 // The work is bound by HBM bandwidth (every valid K/V byte is read once per
 // kv head), so the design keeps many bytes in flight and the arithmetic off
 // the critical path:
-//  * workgroup = (kv head, work item), the items being the 64-page (1024
-//    token) splits of every sequence in order; a workgroup finds its
+//  * workgroup = (kv head, work item), the items being the splits of every
+//    sequence in order (64 pages, 1024 tokens, each; 32 or 16 when that
+//    leaves too few items to fill the chip, e.g. short windows); a workgroup
+//    finds its
 //    (sequence, split) from a prefix sum of the sequences' split counts, so
 //    the dispatch order holds every live item first and the workgroups past
-//    the last item (the grid is sized from max_pages_per_seq, as the host
-//    never reads the device-side lengths) come last and exit at once.  The
+//    the last item (the grid is sized from max_pages_per_seq and the window,
+//    as the host never reads the device-side lengths) come last and exit at
+//    once.  The
 //    4 waves take the split's pages round-robin.  All G <= 16 query heads of
 //    the kv head are processed together, so each K/V byte read serves every
 //    query head of the group (GQA);
@@ -40,7 +43,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kSplitPages = 64;
+constexpr int kMaxSplitPages = 64;   // one page id per lane
+constexpr int kMinSplitPages = 16;   // four pages per wave
+// Items wanted in the grid before the splits are made smaller: about eight
+// workgroups per compute unit.
+constexpr long kTargetItems = 2048;
 constexpr int kD = 128;
 constexpr int kPage = 16;
 constexpr int kRowBytes = kD * 2;
@@ -67,6 +74,7 @@ struct DecArgs {
   const __bf16 *q, *kc, *vc;
   const int32_t *page_table, *seq_lens;
   int n_seq, Hq, Hkv, max_pages, num_pages, max_splits;
+  int split_pages; // pages per split, kMinSplitPages .. kMaxSplitPages
   int window;      // sliding window of the decode query, 0 = none
   float scale_log2;
   ScoreArgs score;
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
       if (i < a.n_seq) {
         int t0, pf, pe;
         key_range(a.seq_lens[i], a.window, a.max_pages, t0, pf, pe);
-        ns = (pe - pf + kSplitPages - 1) / kSplitPages;
+        ns = (pe - pf + a.split_pages - 1) / a.split_pages;
       }
       int incl = ns;
 #pragma unroll
@@ -134,12 +142,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
   int t0, p_first, p_stop;
   key_range(L, a.window, a.max_pages, t0, p_first, p_stop);
   t0 = __builtin_amdgcn_readfirstlane(t0);
-  const int p_begin = __builtin_amdgcn_readfirstlane(p_first + split * kSplitPages);
-  const int p_end = __builtin_amdgcn_readfirstlane(min(p_stop, p_begin + kSplitPages));
+  const int p_begin = __builtin_amdgcn_readfirstlane(p_first + split * a.split_pages);
+  const int p_end = __builtin_amdgcn_readfirstlane(min(p_stop, p_begin + a.split_pages));
   const int qpos = L - 1;
 
   // Page ids of the split, one per lane, read once.
-  static_assert(kSplitPages <= 64, "one page id per lane");
+  static_assert(kMaxSplitPages <= 64, "one page id per lane");
   const int32_t *ptab = a.page_table + (size_t)s * a.max_pages;
   const int my_page = (p_begin + lane < p_end) ? ptab[p_begin + lane] : -1;
 
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
 
 struct CombArgs {
   const int32_t *seq_lens;
-  int Hq, max_pages, max_splits, window;
+  int Hq, max_pages, max_splits, split_pages, window;
   const float *ws_o, *ws_lse;
   __bf16 *out;
   float *lse;
@@ -338,7 +346,7 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(CombArgs a) {
   const int d = threadIdx.x;
   int t0, pf, pe;
   key_range(a.seq_lens[s], a.window, a.max_pages, t0, pf, pe);
-  const int ns = (pe - pf + kSplitPages - 1) / kSplitPages;
+  const int ns = (pe - pf + a.split_pages - 1) / a.split_pages;
   const size_t row0 = ((size_t)s * a.Hq + hq) * a.max_splits;
   float M = -INFINITY;
   for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ws_lse[row0 + k]);
@@ -355,10 +363,24 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(CombArgs a) {
 
 }  // namespace
 
-void decode_split_geometry(int max_pages, int *split_pages, int *max_splits) {
-  *split_pages = kSplitPages;
-  *max_splits = (max_pages + kSplitPages - 1) / kSplitPages;
+int decode_max_splits(int max_pages) { return (max_pages + kMinSplitPages - 1) / kMinSplitPages; }
+
+namespace {
+// Pages a sequence's key range may span: all of max_pages, or under a window
+// of W keys at most (W - 1) / page + 2 (the window need not start on a page
+// boundary).
+int pages_bound(int max_pages, int window) {
+  if (window <= 0) return max_pages;
+  return (int)std::min<long>(max_pages, (long)(window - 1) / kPage + 2);
 }
+// The largest split size that still gives kTargetItems items, assuming every
+// sequence is as long as the bound.
+int choose_split_pages(int n_seq, int Hkv, int bound) {
+  for (int sp = kMaxSplitPages; sp > kMinSplitPages; sp /= 2)
+    if ((long)n_seq * Hkv * ((bound + sp - 1) / sp) >= kTargetItems) return sp;
+  return kMinSplitPages;
+}
+}  // namespace
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
   DecArgs a;
@@ -374,11 +396,16 @@ hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
   a.max_pages = p.max_pages;
   a.num_pages = p.num_pages;
   a.max_splits = p.max_splits;
+  const int bound = pages_bound(p.max_pages, a.window);
+  a.split_pages = choose_split_pages(p.N, p.Hkv, bound);
   a.scale_log2 = p.scale * kLog2e;
   a.score = p.score;
   a.ws_o = p.ws_o;
   a.ws_lse = p.ws_lse;
-  const size_t n_wg = (size_t)p.N * p.max_splits * p.Hkv;
+  // Items that can be live: splits of the longest possible key range.
+  const int splits = (bound + a.split_pages - 1) / a.split_pages;
+  if (splits > p.max_splits) return hipErrorInvalidValue;
+  const size_t n_wg = (size_t)p.N * splits * p.Hkv;
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n_wg);
   hipLaunchKernelGGL(decode_split_kernel, grid, dim3(kThreads), 0, stream, a);
@@ -389,6 +416,7 @@ hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
   c.Hq = p.Hq;
   c.max_pages = p.max_pages;
   c.max_splits = p.max_splits;
+  c.split_pages = a.split_pages;
   c.window = a.window;
   c.ws_o = p.ws_o;
   c.ws_lse = p.ws_lse;

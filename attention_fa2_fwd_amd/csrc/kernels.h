@@ -47,11 +47,11 @@ struct DecodeParams {
   ScoreArgs score;
   float *ws_o;     // [N, Hq, max_splits, D]
   float *ws_lse;   // [N, Hq, max_splits]
-  int max_splits;
-  int split_pages; // pages per split
+  int max_splits;  // split capacity of the workspace per (sequence, head)
 };
-// Split geometry shared by the workspace-size query and the launch.
-void decode_split_geometry(int max_pages, int *split_pages, int *max_splits);
+// Splits per (sequence, head) the workspace must hold: enough for the
+// smallest split size the launch may choose.
+int decode_max_splits(int max_pages);
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);
 
 }  // namespace attn

@@ -147,8 +147,11 @@ int attn_build_block_mask(attn_mask_kind_t mk, const attn_mask_params_t *mp, int
                           int32_t *kv_indices, uint8_t *kv_full, void *stream);
 
 /* attn_paged_decode_workspace_size — bytes of device scratch attn_paged_decode
- * needs for this shape (fp32 partial outputs and log-sum-exps of every key
- * split, sized from max_pages_per_seq so the host never reads seq_lens).   */
+ * needs for this shape: fp32 partial outputs and log-sum-exps of every key
+ * split, for splits as small as 16 pages (the launch takes 64-page splits,
+ * or 32 / 16 when that leaves too few work items), sized from
+ * max_pages_per_seq so the host never reads seq_lens:
+ * N * Hq * ceil(max_pages_per_seq / 16) * (D + 1) * 4 bytes, plus padding. */
 size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int D, int max_pages_per_seq,
                                         int page_size);
 

@@ -122,8 +122,9 @@ def test_paged_decode_checks():
     assert _dec(lib, mk=2, window=100) == -1               # valid mask, null tensors
     assert _dec(lib, N=0) == 0
     assert _dec(lib) == -1                                 # null tensors
-    need = lib.attn_paged_decode_workspace_size(2, 8, 128, 4, 16)
-    # rows = N * Hq * ceil(max_pages / 64); O part rounded up to 256 bytes
-    rows = 2 * 8 * 1
-    assert need == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
+    # rows = N * Hq * ceil(max_pages / 16); O part rounded up to 256 bytes
+    for max_pages, splits in ((4, 1), (16, 1), (17, 2), (300, 19)):
+        need = lib.attn_paged_decode_workspace_size(2, 8, 128, max_pages, 16)
+        rows = 2 * 8 * splits
+        assert need == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
     assert lib.attn_paged_decode_workspace_size(0, 8, 128, 4, 16) == 0

@@ -155,6 +155,18 @@ def test_paged_decode_sliding_window(window):
     run_decode(small_decode_inputs(LENGTHS, seed=5), "alibi", "window", window=window)
 
 
+@pytest.mark.parametrize("n_seq,window,split", [(64, 0, 64), (40, 0, 32), (40, 700, 16)])
+def test_paged_decode_split_sizes(n_seq, window, split):
+    # The launch takes 64-, 32- or 16-page splits depending on how many work
+    # items the sequence count, the kv heads and the longest key range give
+    # (2048 wanted); these shapes land on each size in turn.
+    rng = np.random.default_rng(n_seq + window)
+    lengths = rng.integers(1, 300 * 16 + 1, size=n_seq)
+    lengths[:3] = [0, 1, 300 * 16]
+    inp = small_decode_inputs(list(lengths), hq=8, hkv=8, max_pages=300, seed=7)
+    run_decode(inp, "alibi", f"split {split}", window=window)
+
+
 def test_paged_decode_window_skips_pages_before_it():
     # NaN in every slot before each sequence's window: pages wholly before the
     # window are never read, and the keys of the first page that precede the

@@ -22,7 +22,7 @@ are lost, so each reading taken is stated where it is used):
   ``score_mod(score, b, h, q_idx, kv_idx)`` applied before softmax, and the
   five-deep loop that defines it); §全注意力 (identity score_mod);
   §相对位置编码 (bias from the query-key distance, computed in-kernel);
-  §Causal Mask; §Sliding Window + Causal (the most recent 1024 tokens).
+  §Soft-capping (named, formula lost); §Causal Mask; §Sliding Window + Causal (the most recent 1024 tokens).
 * [Online-Softmax page] "Attention优化｜2w字原理&图解: 从Online-Softmax到
   FlashAttention V1/V2/V3", abstract: 3-pass safe softmax, 2-pass online
   softmax and 1-pass FlashAttention are forms of one result.
@@ -39,9 +39,9 @@ invariants, library cross-checks); none is "parity unpinned".
 
 from .attention import (  # noqa: F401
     MASK_NONE, MASK_CAUSAL, MASK_SLIDING, MASK_PREFIX_LM, MASK_DOCUMENT,
-    SCORE_NONE, SCORE_ALIBI, SCORE_REL_POS,
+    SCORE_NONE, SCORE_ALIBI, SCORE_REL_POS, SCORE_SOFTCAP,
     MaskSpec, ScoreSpec,
-    alibi_slopes, visible, bias, scores_block, kv_head,
+    alibi_slopes, visible, bias, score_mod, scores_block, kv_head,
     softmax_naive, softmax_safe3, softmax_online2,
     attention_rows, attention_ref, attention_bruteforce, attention_one_pass,
 )

@@ -10,7 +10,8 @@ the softmax):
 
     hkv       = floor(hq * Hkv / Hq)                      (GQA head map)
     S[i, j]   = s * sum_d Q[b,hq,i,d] * K[b,hkv,j,d]       (s = fp32 scale)
-    S[i, j]  += bias(hq, i, j)                            (score_mod kind)
+    S[i, j]   = score_mod(S[i, j], hq, i, j)              (score_mod kind:
+                S + bias(hq, i, j), or cap * tanh(S / cap))
     S[i, j]   = -inf where not visible(b, i, j)           (mask kind)
     P[i, :]   = softmax(S[i, :])                          (3-pass safe form)
     O[i, :]   = sum_j P[i, j] * V[b,hkv,j,:]
@@ -24,6 +25,11 @@ Readings taken where the pages are silent (their formulas were images):
   query head (the variant is only named in the page's list);
 * relative position adds c * (i - j) (§相对位置编码: the score is adjusted by
   the query-key distance; c is a per-call constant, default 1);
+* soft-capping maps the scaled score x to cap * tanh(x / cap), cap > 0 a
+  per-call constant (§Soft-capping names the technique, used by Gemma 2 and
+  Grok-1, but its formula did not survive; this is the usual definition: a
+  smooth, odd, increasing squashing of every score into (-cap, cap) that is
+  the identity to first order);
 * causal is inclusive, j <= i (§Causal Mask: each token attends to the tokens
   before it; row 0 then returns V[0]);
 * the sliding window keeps exactly W keys, self included: 0 <= i - j < W
@@ -50,6 +56,7 @@ MASK_DOCUMENT = 4      # causal within a document
 SCORE_NONE = 0
 SCORE_ALIBI = 1
 SCORE_REL_POS = 2
+SCORE_SOFTCAP = 3
 
 
 @dataclass(frozen=True)
@@ -65,6 +72,7 @@ class ScoreSpec:
     kind: int = SCORE_NONE
     slopes: Optional[np.ndarray] = None   # [Hq]; None -> alibi_slopes(Hq)
     rel_scale: float = 1.0
+    softcap: float = 0.0                  # SOFTCAP: the cap, > 0
 
 
 def alibi_slopes(hq_count: int) -> np.ndarray:
@@ -113,7 +121,24 @@ def bias(score: ScoreSpec, hq: int, hq_count: int, i, j):
         return slopes[hq] * (j - i)
     if score.kind == SCORE_REL_POS:
         return float(score.rel_scale) * (i - j)
+    if score.kind == SCORE_SOFTCAP:
+        raise ValueError("soft-capping is not an additive bias")
     raise ValueError(f"unknown score kind {score.kind}")
+
+
+def score_mod(score: ScoreSpec, s, hq: int, hq_count: int, i, j) -> np.ndarray:
+    """The modified scores score_mod(S) of a block S[len(i), len(j)].
+
+    [FlexAttention page] §FlexAttention (every score passes through score_mod
+    before the softmax).  Additive kinds add bias(); SOFTCAP returns
+    cap * tanh(S / cap) (§Soft-capping).
+    """
+    if score.kind == SCORE_SOFTCAP:
+        cap = float(score.softcap)
+        if not cap > 0.0:
+            raise ValueError("soft-capping needs cap > 0")
+        return cap * np.tanh(np.asarray(s, dtype=np.float64) / cap)
+    return s + bias(score, hq, hq_count, i, j)
 
 
 def kv_head(hq: int, hq_count: int, hkv_count: int) -> int:
@@ -132,14 +157,14 @@ def scores_block(q_rows, k, scale, mask: MaskSpec, score: ScoreSpec,
     """Materialised modified scores S[i, j] for the given query rows.
 
     q_rows: [n, D] (rows row_idx of Q[b, hq]); k: [m, D] (keys col_idx).
-    Order: scale, then bias, then mask (-inf where not visible).
+    Order: scale, then score_mod, then mask (-inf where not visible).
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     row_idx = np.asarray(row_idx, dtype=np.int64)
     col_idx = np.arange(k.shape[0]) if col_idx is None else np.asarray(col_idx, np.int64)
     s = _fp32_scale(scale) * (q_rows @ k.T)
-    s = s + bias(score, hq, hq_count, row_idx, col_idx)
+    s = score_mod(score, s, hq, hq_count, row_idx, col_idx)
     vis = visible(mask, b, row_idx, col_idx)
     return np.where(vis, s, -np.inf)
 
@@ -268,11 +293,13 @@ def attention_bruteforce(q, k, v, scale, mask: MaskSpec = MaskSpec(),
             slopes = [float(x) for x in score.slopes]
     doc = None if mask.doc_ids is None else np.asarray(mask.doc_ids).tolist()
 
-    def score_mod(x, b, h, qi, kj):
+    def score_mod_1(x, b, h, qi, kj):
         if score.kind == SCORE_ALIBI:
             x = x + slopes[h] * (kj - qi)
         elif score.kind == SCORE_REL_POS:
             x = x + float(score.rel_scale) * (qi - kj)
+        elif score.kind == SCORE_SOFTCAP:
+            x = float(score.softcap) * math.tanh(x / float(score.softcap))
         return x
 
     def is_visible(b, qi, kj):
@@ -299,7 +326,7 @@ def attention_bruteforce(q, k, v, scale, mask: MaskSpec = MaskSpec(),
                     dot = 0.0
                     for t in range(d):
                         dot += q[b][h][qi][t] * k[b][g][kj][t]
-                    x = score_mod(s_fp * dot, b, h, qi, kj)
+                    x = score_mod_1(s_fp * dot, b, h, qi, kj)
                     row.append(x if is_visible(b, qi, kj) else None)
                 live = [x for x in row if x is not None]
                 if not live:

@@ -20,7 +20,7 @@ import test_oracle_blockmask_decode as bpins
 def _all_pins():
     pins.check_softmax_forms()
     for mi, mask in enumerate(pins.all_masks(16)):
-        for si, score in enumerate(pins.ALL_SCORES):
+        for si, score in enumerate(pins.ALL_MODS):
             pins.check_bruteforce(mask, score, seed=mi * 3 + si)
     pins.check_causal_row0_and_q0()
     pins.check_window_closed_forms()
@@ -29,6 +29,7 @@ def _all_pins():
     pins.check_alibi_closed_form()
     pins.check_alibi_closed_form(window=7)
     pins.check_rel_pos_closed_form()
+    pins.check_softcap_closed_forms()
     pins.check_value_special_cases()
     pins.check_invariances()
     for mi in range(5):
@@ -71,6 +72,25 @@ def _document_not_causal(mask, b, i, j):
     return _orig_visible(mask, b, i, j)
 
 
+def _softcap_no_inner_division(score, s, hq, hq_count, i, j):
+    if score.kind == att.SCORE_SOFTCAP:
+        return score.softcap * np.tanh(s)
+    return _orig_score_mod(score, s, hq, hq_count, i, j)
+
+
+def _softcap_no_outer_factor(score, s, hq, hq_count, i, j):
+    if score.kind == att.SCORE_SOFTCAP:
+        return np.tanh(s / score.softcap)
+    return _orig_score_mod(score, s, hq, hq_count, i, j)
+
+
+def _softcap_clip(score, s, hq, hq_count, i, j):
+    # a hard clip instead of the smooth cap
+    if score.kind == att.SCORE_SOFTCAP:
+        return np.clip(s, -score.softcap, score.softcap)
+    return _orig_score_mod(score, s, hq, hq_count, i, j)
+
+
 def _wrong_head_map(hq, hq_count, hkv_count):
     return hq % hkv_count
 
@@ -92,6 +112,7 @@ def _transposed_scores(q_rows, k, scale, mask, score, b, hq, hq_count, row_idx, 
 
 
 _orig_bias = att.bias
+_orig_score_mod = att.score_mod
 _orig_visible = att.visible
 _orig_scores = att.scores_block
 
@@ -105,6 +126,9 @@ MUTATIONS = {
     "dropped_scale": ("_fp32_scale", _no_scale),
     "no_max_shift": ("softmax_safe3", _no_max_shift),
     "transposed_scores": ("scores_block", _transposed_scores),
+    "softcap_no_inner_division": ("score_mod", _softcap_no_inner_division),
+    "softcap_no_outer_factor": ("score_mod", _softcap_no_outer_factor),
+    "softcap_hard_clip": ("score_mod", _softcap_clip),
 }
 
 

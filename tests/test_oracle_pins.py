@@ -18,7 +18,8 @@ import torch
 import oracle
 from oracle import attention as att
 from oracle import (MaskSpec, ScoreSpec, MASK_NONE, MASK_CAUSAL, MASK_SLIDING,
-                    MASK_PREFIX_LM, MASK_DOCUMENT, SCORE_NONE, SCORE_ALIBI, SCORE_REL_POS)
+                    MASK_PREFIX_LM, MASK_DOCUMENT, SCORE_NONE, SCORE_ALIBI, SCORE_REL_POS,
+                    SCORE_SOFTCAP)
 
 RNG = np.random.default_rng(1234)
 
@@ -43,6 +44,8 @@ def all_masks(s, lengths=None):
 
 
 ALL_SCORES = [ScoreSpec(SCORE_NONE), ScoreSpec(SCORE_ALIBI), ScoreSpec(SCORE_REL_POS, rel_scale=-0.3)]
+# every modifier kind: the additive ones above and soft-capping
+ALL_MODS = ALL_SCORES + [ScoreSpec(SCORE_SOFTCAP, softcap=0.75)]
 
 
 # ----------------------------------------------------------------------------
@@ -89,9 +92,9 @@ def check_bruteforce(mask, score, seed=0):
 
 
 @pytest.mark.parametrize("mi", range(5))
-@pytest.mark.parametrize("si", range(3))
+@pytest.mark.parametrize("si", range(4))
 def test_bruteforce_matches_vectorised(mi, si):
-    check_bruteforce(all_masks(16)[mi], ALL_SCORES[si], seed=10 * mi + si)
+    check_bruteforce(all_masks(16)[mi], ALL_MODS[si], seed=10 * mi + si)
 
 
 def test_bruteforce_rectangular_none_mask():
@@ -112,7 +115,7 @@ def test_one_pass_matches_three_pass(mi):
     b, hq, hkv, s, d = 2, 4, 2, 37, 8
     q, k, v = rand(b, hq, s, d, rng=rng), rand(b, hkv, s, d, rng=rng), rand(b, hkv, s, d, rng=rng)
     mask = all_masks(s, [10, 20, 7])[mi]
-    for score in ALL_SCORES:
+    for score in ALL_MODS:
         o3, l3 = oracle.attention_ref(q, k, v, 0.4, mask, score)
         o1, l1 = oracle.attention_one_pass(q, k, v, 0.4, mask, score, kv_tile=8)
         np.testing.assert_allclose(o1, o3, atol=1e-13)
@@ -293,6 +296,56 @@ def test_rel_pos_closed_form():
     check_rel_pos_closed_form()
 
 
+def check_softcap_closed_forms():
+    # [FlexAttention page] §Soft-capping, read as x -> cap * tanh(x / cap).
+    # (1) Two keys whose scaled scores are cap * artanh(+-y), y = a / cap:
+    # the capped scores are +-a; with a = ln(3) / 2 the weights are exactly
+    # 3/4 and 1/4 and LSE = ln(e^a + e^-a) = ln(4 / sqrt 3).  Scale 0.5 and
+    # D = 4, so a cap applied before the scale, or without the inner division
+    # or the outer factor, lands elsewhere.
+    a = math.log(3.0) / 2.0
+    for cap in (0.6, 4.0):
+        x = cap * math.atanh(a / cap)
+        q = np.zeros((1, 1, 2, 4))
+        q[0, 0, :, 0] = 1.0
+        k = np.zeros((1, 1, 2, 4))
+        k[0, 0, 0, 0] = 2.0 * x                    # scale 0.5 -> +x
+        k[0, 0, 1, 0] = -2.0 * x                   # -> -x
+        v = np.array([[[[1.0, 0.0, 2.0], [0.0, 1.0, -2.0]]]])
+        o, lse = oracle.attention_ref(q, k, v, 0.5, MaskSpec(MASK_NONE), ScoreSpec(SCORE_SOFTCAP, softcap=cap))
+        for i in range(2):
+            np.testing.assert_allclose(o[0, 0, i], [0.75, 0.25, 1.0], atol=1e-13)
+            assert lse[0, 0, i] == pytest.approx(math.log(4.0 / math.sqrt(3.0)), abs=1e-13)
+    rng = np.random.default_rng(57)
+    s, d = 23, 8
+    q, k, v = rand(1, 2, s, d, rng=rng), rand(1, 2, s, d, rng=rng), rand(1, 2, s, d, rng=rng)
+    i = np.arange(s)
+    # (2) a vanishing cap squashes every score to 0: uniform weights over the
+    # visible keys, O = their mean and LSE = ln(count)
+    o, lse = oracle.attention_ref(q, k, v, 3.0, MaskSpec(MASK_CAUSAL), ScoreSpec(SCORE_SOFTCAP, softcap=1e-9))
+    np.testing.assert_allclose(lse[0, 0], np.log(i + 1.0), atol=1e-8)
+    np.testing.assert_allclose(o[0, 0], np.cumsum(v[0, 0], axis=0) / (i + 1.0)[:, None], atol=1e-8)
+    # (3) a cap far above every score leaves the scores unchanged
+    o1, l1 = oracle.attention_ref(q, k, v, 0.4, MaskSpec(MASK_SLIDING, window=5),
+                                  ScoreSpec(SCORE_SOFTCAP, softcap=1e7))
+    o0, l0 = oracle.attention_ref(q, k, v, 0.4, MaskSpec(MASK_SLIDING, window=5))
+    np.testing.assert_allclose(o1, o0, atol=1e-11)
+    np.testing.assert_allclose(l1, l0, atol=1e-11)
+    # (4) capped scores lie in [-cap, cap] (equal only where tanh rounds to
+    # +-1) and never reverse the order of the raw ones
+    for sc in (5.0, 0.3):
+        raw = oracle.scores_block(q[0, 0], k[0, 0], sc, MaskSpec(MASK_NONE), ScoreSpec(), 0, 0, 2, i)
+        cap = oracle.scores_block(q[0, 0], k[0, 0], sc, MaskSpec(MASK_NONE),
+                                  ScoreSpec(SCORE_SOFTCAP, softcap=1.5), 0, 0, 2, i)
+        assert np.all(np.abs(cap) <= 1.5)
+        order = np.argsort(raw, axis=1)
+        assert np.all(np.diff(np.take_along_axis(cap, order, axis=1), axis=1) >= 0.0)
+
+
+def test_softcap_closed_forms():
+    check_softcap_closed_forms()
+
+
 def check_value_special_cases():
     rng = np.random.default_rng(31)
     s, d = 21, 5
@@ -300,7 +353,7 @@ def check_value_special_cases():
     row = rand(d, rng=rng)
     vconst = np.broadcast_to(row, (2, 2, s, d)).copy()
     for mask in all_masks(s, [6, 6, 9]):
-        for score in ALL_SCORES:
+        for score in ALL_MODS:
             o, _ = oracle.attention_ref(q, k, vconst, 0.3, mask, score)
             np.testing.assert_allclose(o, np.broadcast_to(row, o.shape), atol=1e-14)
     v = rand(2, 2, s, d, rng=rng)

@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libattn_fa2.so")
 
 F32, BF16 = 0, 1
 MASK_KINDS = {"none": 0, "causal": 1, "sliding": 2, "prefix_lm": 3, "document": 4}
-SCORE_KINDS = {"none": 0, "alibi": 1, "rel_pos": 2}
+SCORE_KINDS = {"none": 0, "alibi": 1, "rel_pos": 2, "softcap": 3}
 EXPORTED = ("attn_fwd", "attn_build_block_mask", "attn_paged_decode_workspace_size",
             "attn_paged_decode", "attn_last_error")
 
@@ -45,7 +45,8 @@ class MaskParams(ctypes.Structure):
 
 
 class ScoreParams(ctypes.Structure):
-    _fields_ = [("alibi_slopes", ctypes.c_void_p), ("rel_scale", ctypes.c_float)]
+    _fields_ = [("alibi_slopes", ctypes.c_void_p), ("rel_scale", ctypes.c_float),
+                ("softcap", ctypes.c_float)]
 
 
 class BlockMaskC(ctypes.Structure):
@@ -129,18 +130,19 @@ def _mask_params(mask: str, window: int, prefix_len: int, doc_ids: Optional[torc
     return MASK_KINDS[mask], MaskParams(int(window), int(prefix_len), _ptr(doc_ids))
 
 
-def _score_params(score: str, alibi_slopes: Optional[torch.Tensor], rel_scale: float):
+def _score_params(score: str, alibi_slopes: Optional[torch.Tensor], rel_scale: float,
+                  softcap: float):
     if score not in SCORE_KINDS:
         raise ValueError(f"unknown score kind {score!r}")
     if alibi_slopes is not None and alibi_slopes.dtype != torch.float32:
         raise ValueError("alibi_slopes must be float32")
-    return SCORE_KINDS[score], ScoreParams(_ptr(alibi_slopes), float(rel_scale))
+    return SCORE_KINDS[score], ScoreParams(_ptr(alibi_slopes), float(rel_scale), float(softcap))
 
 
 def attn_fwd(q, k, v, *, scale: Optional[float] = None, mask: str = "none", window: int = 0,
              prefix_len: int = 0, doc_ids=None, score: str = "none", alibi_slopes=None,
-             rel_scale: float = 1.0, block_mask: Optional[BlockMask] = None, out=None, lse=None,
-             out_dtype=None):
+             rel_scale: float = 1.0, softcap: float = 0.0, block_mask: Optional[BlockMask] = None,
+             out=None, lse=None, out_dtype=None):
     """Fused attention forward.  q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] (bf16 or fp32).
     Returns (out [B,Hq,Sq,D], lse [B,Hq,Sq] float32).  out_dtype defaults to
     the input dtype; torch.float32 gives bf16 inputs an fp32 output."""
@@ -159,7 +161,7 @@ def attn_fwd(q, k, v, *, scale: Optional[float] = None, mask: str = "none", wind
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     mk, mp = _mask_params(mask, window, prefix_len, doc_ids)
-    sk, sp = _score_params(score, alibi_slopes, rel_scale)
+    sk, sp = _score_params(score, alibi_slopes, rel_scale, softcap)
     bmc = block_mask.to_c() if block_mask is not None else None
     rc = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                       BF16 if q.dtype == torch.bfloat16 else F32,
@@ -197,7 +199,8 @@ def attn_paged_decode_workspace_size(num_seqs: int, Hq: int, D: int, max_pages_p
 
 def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optional[float] = None,
                       mask: str = "none", window: int = 0, score: str = "none", alibi_slopes=None,
-                      rel_scale: float = 1.0, workspace=None, out=None, lse=None):
+                      rel_scale: float = 1.0, softcap: float = 0.0, workspace=None, out=None,
+                      lse=None):
     """Paged split-KV decode.  q [N,Hq,D] bf16; caches [pages,Hkv,page,D] bf16;
     page_table int32 [N,max_pages]; seq_lens int32 [N]; mask "none" or
     "sliding" (the query at seq_lens-1 sees the last `window` keys).
@@ -220,7 +223,7 @@ def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optio
     _need_device(q, k_cache, v_cache, page_table, seq_lens, out, lse, workspace, alibi_slopes)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    sk, sp = _score_params(score, alibi_slopes, rel_scale)
+    sk, sp = _score_params(score, alibi_slopes, rel_scale, softcap)
     if mask not in MASK_KINDS:
         raise ValueError(f"unknown mask {mask!r}")
     mp = MaskParams(int(window), 0, None)

@@ -1,6 +1,7 @@
 // C ABI of the attention library: argument validation, kernel selection and
 // launch on the caller's stream.  Every check runs on the host before any
 // launch; the library allocates nothing and never synchronises.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -20,7 +21,7 @@ int fail(int code, const char *fmt, ...) {
 }
 
 bool valid_mask_kind(int mk) { return mk >= ATTN_MASK_NONE && mk <= ATTN_MASK_DOCUMENT; }
-bool valid_score_kind(int sk) { return sk >= ATTN_SCORE_NONE && sk <= ATTN_SCORE_REL_POS; }
+bool valid_score_kind(int sk) { return sk >= ATTN_SCORE_NONE && sk <= ATTN_SCORE_SOFTCAP; }
 
 // Shared checks of mask parameters; fills the kernel-side copy.
 int check_mask(int mk, const attn_mask_params_t *mp, int Sq, int Skv, attn::MaskArgs *out) {
@@ -51,7 +52,13 @@ int check_score(int sk, const attn_score_params_t *sp, attn::ScoreArgs *out) {
   out->kind = sk;
   out->slopes = sp ? sp->alibi_slopes : nullptr;
   out->rel_scale = sp ? sp->rel_scale : 1.0f;
+  out->softcap = sp ? sp->softcap : 0.0f;
   if (sk == ATTN_SCORE_REL_POS && !sp) return fail(ATTN_ERR_INVALID, "REL_POS needs score params");
+  if (sk == ATTN_SCORE_SOFTCAP) {
+    if (!sp) return fail(ATTN_ERR_INVALID, "SOFTCAP needs score params");
+    if (!(sp->softcap > 0.0f) || !std::isfinite(sp->softcap))
+      return fail(ATTN_ERR_INVALID, "SOFTCAP needs a finite cap > 0 (got %g)", (double)sp->softcap);
+  }
   return ATTN_OK;
 }
 

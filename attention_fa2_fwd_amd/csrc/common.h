@@ -42,6 +42,7 @@ struct ScoreArgs {
   int kind;
   const float *slopes;
   float rel_scale;
+  float softcap;   // SOFTCAP: the cap, > 0
 };
 
 // visible(b, i, j) of the mask kind.  doc_i is doc_ids[b, i] (read once per
@@ -73,6 +74,16 @@ __device__ __forceinline__ float bias_coeff(const ScoreArgs &s, int hq, int Hq) 
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Soft-capping of a log2-domain score x = s * log2(e): C tanh(x / C) with
+// C = cap * log2(e), written as C - 2C / (1 + 2^(kx)), k = 2 / cap (since
+// e^(2x/C) = 2^(2x/cap)).  k_scaled = k * c folds in a prior multiply x = c s.
+// Saturates to +-C without overflow (2^(kx) = inf gives C, 0 gives -C).  The
+// hardware exp2 and reciprocal leave an absolute error of a few C * 2^-24.
+__device__ __forceinline__ float softcap_log2_fast(float s, float k_scaled, float C) {
+  const float e = fast_exp2(s * k_scaled);
+  return __builtin_fmaf(-2.0f * C, __builtin_amdgcn_rcpf(1.0f + e), C);
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Max / sum of a value across the two 32-lane halves of a wave64, broadcast

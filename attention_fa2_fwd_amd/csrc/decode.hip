@@ -160,7 +160,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
     if (col < G) qf[c] = *(const bf16x8 *)(a.q + ((size_t)s * a.Hq + hq0 + col) * kD + 32 * c + 8 * grp);
   }
   const float bias2 = (col < G) ? bias_coeff(a.score, hq0 + col, a.Hq) * kLog2e : 0.0f;
-  const bool has_bias = a.score.kind != ATTN_SCORE_NONE;
+  const bool has_bias = a.score.kind == ATTN_SCORE_ALIBI || a.score.kind == ATTN_SCORE_REL_POS;
+  const bool has_cap = a.score.kind == ATTN_SCORE_SOFTCAP;
+  const float cap2 = has_cap ? a.score.softcap * kLog2e : 0.0f;
+  const float cap_k = has_cap ? 2.0f / a.score.softcap : 0.0f;
 
   // O^T accumulators: o[blk][i] = O[head col][d = 16 blk + 4 grp + i].
   f32x4 o[8];
@@ -224,6 +227,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
     for (int i = 0; i < 4; ++i) {
       float v = sacc[i] * a.scale_log2;
       if (has_bias) v = __builtin_fmaf(bias2, (float)(j0 + i - qpos), v);
+      if (has_cap) v = softcap_log2_fast(v, cap_k, cap2);
       x[i] = (j0 + i < L && j0 + i >= t0) ? v : -INFINITY;
     }
     float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));

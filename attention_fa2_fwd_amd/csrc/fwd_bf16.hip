@@ -97,13 +97,21 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }
 
-// Compile-time variants: D, the mask kind, GEN (materialise the modified
-// score x = c*s + bias before the max: needed for a bias or a scale <= 0) and
-// the output dtype.  Without GEN the row max is taken on the raw dot products
-// (c > 0 preserves order) and p = 2^(c*s - m) is one FMA and one exp2.
-template <int D, int MASK, bool GEN, bool OUT_F32>
+// How the log2-domain score x is formed from the dot product s:
+//  kModRaw   x = c s, never materialised: the row max is taken on the raw dot
+//            products (c > 0 preserves order) and p = 2^(c s - m) is one FMA
+//            and one exp2;
+//  kModBias  x = c s + bias, materialised before the max (any bias, or a
+//            scale <= 0);
+//  kModCap   x = C tanh(c s / C), the soft cap, materialised before the max.
+constexpr int kModRaw = 0, kModBias = 1, kModCap = 2;
+
+// Compile-time variants: D, the mask kind, the score form MOD and the output
+// dtype.
+template <int D, int MASK, int MOD, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   using C = FwdCfg<D>;
+  constexpr bool GEN = MOD != kModRaw;   // x materialised before the max
   // K and V double buffers as four distinct LDS objects, always addressed
   // through their own names: the compiler can then tell that reading one
   // buffer does not depend on buffer->LDS loads still in flight to another,
@@ -268,7 +276,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   for (int i = 0; i < C::NDB; ++i) o[i] = f32x16{};
 
   const float c_log2 = a.scale_log2;
-  const float bias2 = GEN ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
+  const float bias2 = (MOD == kModBias) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
+  // Soft cap in log2 units and its exponent factor (2 / cap) * c.
+  const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
+  const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
   const int doc_i = (MASK == ATTN_MASK_DOCUMENT) ? doc_row[min(qi, a.Sq - 1)] : 0;
   asm volatile("" ::"v"(doc_i));   // complete the load before the tile loop
 
@@ -311,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     // Accumulator element r of block kb is key j = jb + kb*32 + 8(r/4) + r%4
     // with jb = k0 + 4h.
     const int jb = k0 + 4 * h;
-    if constexpr (GEN) {
+    if constexpr (MOD == kModBias) {
       const float cb = bias2 * (float)(jb - qi);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -320,6 +331,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
           const float off = (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
           s[kb][r] = __builtin_fmaf(s[kb][r], c_log2, __builtin_fmaf(bias2, off, cb));
         }
+    } else if constexpr (MOD == kModCap) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = softcap_log2_fast(s[kb][r], cap_k, cap2);
     }
     if (!full) {
       // Partial tile: the mask predicate per element; -inf where hidden (for
@@ -525,20 +541,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   }
 }
 
-template <int D, int MASK, bool GEN, bool OUT_F32>
+template <int D, int MASK, int MOD, bool OUT_F32>
 hipError_t launch_variant(const KernelArgs &a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, GEN, OUT_F32>), dim3(grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, MOD, OUT_F32>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool GEN, bool OUT_F32>
+template <int D, int MOD, bool OUT_F32>
 hipError_t launch_mask(const KernelArgs &a, int mask, unsigned grid, hipStream_t stream) {
   switch (mask) {
-    case ATTN_MASK_NONE: return launch_variant<D, ATTN_MASK_NONE, GEN, OUT_F32>(a, grid, stream);
-    case ATTN_MASK_CAUSAL: return launch_variant<D, ATTN_MASK_CAUSAL, GEN, OUT_F32>(a, grid, stream);
-    case ATTN_MASK_SLIDING: return launch_variant<D, ATTN_MASK_SLIDING, GEN, OUT_F32>(a, grid, stream);
-    case ATTN_MASK_PREFIX_LM: return launch_variant<D, ATTN_MASK_PREFIX_LM, GEN, OUT_F32>(a, grid, stream);
-    case ATTN_MASK_DOCUMENT: return launch_variant<D, ATTN_MASK_DOCUMENT, GEN, OUT_F32>(a, grid, stream);
+    case ATTN_MASK_NONE: return launch_variant<D, ATTN_MASK_NONE, MOD, OUT_F32>(a, grid, stream);
+    case ATTN_MASK_CAUSAL: return launch_variant<D, ATTN_MASK_CAUSAL, MOD, OUT_F32>(a, grid, stream);
+    case ATTN_MASK_SLIDING: return launch_variant<D, ATTN_MASK_SLIDING, MOD, OUT_F32>(a, grid, stream);
+    case ATTN_MASK_PREFIX_LM: return launch_variant<D, ATTN_MASK_PREFIX_LM, MOD, OUT_F32>(a, grid, stream);
+    case ATTN_MASK_DOCUMENT: return launch_variant<D, ATTN_MASK_DOCUMENT, MOD, OUT_F32>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -568,14 +584,17 @@ hipError_t launch_d(const FwdParams &p, hipStream_t stream) {
   a.bm_batch = p.bm_batch;
   a.tiles_per_block = p.bm_num ? p.bm_kv_block / kBN : 1;
   const unsigned grid = (unsigned)(a.n_qtiles * p.B * p.Hq);
-  // The raw-score path needs a positive scale and no bias.
-  const bool gen = (p.score.kind != ATTN_SCORE_NONE) || !(a.scale_log2 > 0.0f);
-  if (gen) {
-    return p.out_f32 ? launch_mask<D, true, true>(a, p.mask.kind, grid, stream)
-                     : launch_mask<D, true, false>(a, p.mask.kind, grid, stream);
+  if (p.score.kind == ATTN_SCORE_SOFTCAP) {
+    return p.out_f32 ? launch_mask<D, kModCap, true>(a, p.mask.kind, grid, stream)
+                     : launch_mask<D, kModCap, false>(a, p.mask.kind, grid, stream);
   }
-  return p.out_f32 ? launch_mask<D, false, true>(a, p.mask.kind, grid, stream)
-                   : launch_mask<D, false, false>(a, p.mask.kind, grid, stream);
+  // The raw-score path needs a positive scale and no bias.
+  if (p.score.kind != ATTN_SCORE_NONE || !(a.scale_log2 > 0.0f)) {
+    return p.out_f32 ? launch_mask<D, kModBias, true>(a, p.mask.kind, grid, stream)
+                     : launch_mask<D, kModBias, false>(a, p.mask.kind, grid, stream);
+  }
+  return p.out_f32 ? launch_mask<D, kModRaw, true>(a, p.mask.kind, grid, stream)
+                   : launch_mask<D, kModRaw, false>(a, p.mask.kind, grid, stream);
 }
 
 }  // namespace

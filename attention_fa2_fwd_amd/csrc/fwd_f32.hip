@@ -58,7 +58,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
 
   const int mk = a.mask.kind;
   const float bias2 = bias_coeff(a.score, hq, a.Hq) * kLog2e;
-  const bool has_bias = a.score.kind != ATTN_SCORE_NONE;
+  const bool has_bias = a.score.kind == ATTN_SCORE_ALIBI || a.score.kind == ATTN_SCORE_REL_POS;
+  const bool has_cap = a.score.kind == ATTN_SCORE_SOFTCAP;
+  const float cap2 = a.score.softcap * kLog2e;   // the cap in log2 units
   const int32_t *doc_row = (mk == ATTN_MASK_DOCUMENT) ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride
                                                       : nullptr;
   const int doc_i = (doc_row && row_ok) ? doc_row[qi] : -1;
@@ -110,6 +112,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
         part += __shfl_xor(part, 2);
         float x = part * a.scale_log2;
         if (has_bias) x += bias2 * (float)(j - qi);
+        if (has_cap) x = cap2 * tanhf(x / cap2);   // cap tanh(s / cap), in log2 units
         const bool vis = mask_visible(a.mask, qi, j, doc_i, doc_row);
         if (!vis) continue;
         if (x > m_run) {

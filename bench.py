@@ -101,7 +101,7 @@ def bench_prefill(af, torch, workloads, w, steps, warmup, out_dtype=None, with_b
     out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     kw = dict(scale=1.0 / math.sqrt(w.D), mask=w.mask, window=w.window, prefix_len=w.prefix_len,
-              doc_ids=doc, score=w.score, block_mask=bm, out=out, lse=lse)
+              doc_ids=doc, score=w.score, softcap=w.softcap, block_mask=bm, out=out, lse=lse)
     for _ in range(warmup):
         af.attn_fwd(q, k, v, **kw)
     torch.cuda.synchronize()
@@ -196,7 +196,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="run one workload (dense, causal, gqa, document, decode, decode_window) and exit")
+                    help="run one workload (dense, causal, gqa, document, causal_softcap, decode, "
+                         "decode_window) and exit")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy, to calibrate byte counters")
     args = ap.parse_args()
@@ -228,7 +229,8 @@ def main():
 
     if args.only:
         sel = {"dense": workloads.DENSE_BF16, "causal": workloads.CAUSAL_BF16,
-               "gqa": workloads.GQA_WINDOW_ALIBI, "document": workloads.DOCUMENT_BLOCKMASK}
+               "gqa": workloads.GQA_WINDOW_ALIBI, "document": workloads.DOCUMENT_BLOCKMASK,
+               "causal_softcap": workloads.CAUSAL_SOFTCAP}
         if args.only == "decode":
             r = bench_decode(af, torch, workloads, args.steps, args.warmup)
         elif args.only == "decode_window":
@@ -319,7 +321,8 @@ def main():
     if not args.no_extra:
         extra = {}
         for name, w in (("gqa_window1024_alibi", workloads.GQA_WINDOW_ALIBI),
-                        ("document_blockmask", workloads.DOCUMENT_BLOCKMASK)):
+                        ("document_blockmask", workloads.DOCUMENT_BLOCKMASK),
+                        ("causal_softcap5", workloads.CAUSAL_SOFTCAP)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             extra[name] = bench_prefill(af, torch, workloads, w, 20, 3)
         print("[bench] paged decode", file=sys.stderr, flush=True)

@@ -71,22 +71,26 @@ typedef struct {
   const int32_t *doc_ids;  /* DOCUMENT: device int32 [B, S] (Sq == Skv == S) */
 } attn_mask_params_t;
 
-/* Score modifiers, added to the scaled score before the mask and softmax
- * (FlexAttention write-up §相对位置编码: a bias from the query-key distance
- * computed inside the kernel, never stored as an S x S tensor; ALiBi from the
- * variant list):
- *   NONE     0
- *   ALIBI    slope[hq] * (j - i),  slope[h] = 2^(-8 (h+1) / Hq) by default
- *   REL_POS  rel_scale * (i - j)                                             */
+/* Score modifiers, applied to the scaled score x = scale * q.k before the
+ * mask and softmax (FlexAttention write-up §FlexAttention: score_mod on every
+ * score; §相对位置编码: a bias from the query-key distance computed inside
+ * the kernel, never stored as an S x S tensor; ALiBi from the variant list;
+ * §Soft-capping, formula lost, read as below):
+ *   NONE     x
+ *   ALIBI    x + slope[hq] * (j - i),  slope[h] = 2^(-8 (h+1) / Hq) by default
+ *   REL_POS  x + rel_scale * (i - j)
+ *   SOFTCAP  softcap * tanh(x / softcap), softcap > 0 and finite            */
 typedef enum {
   ATTN_SCORE_NONE = 0,
   ATTN_SCORE_ALIBI = 1,
-  ATTN_SCORE_REL_POS = 2
+  ATTN_SCORE_REL_POS = 2,
+  ATTN_SCORE_SOFTCAP = 3
 } attn_score_kind_t;
 
 typedef struct {
   const float *alibi_slopes; /* device float [Hq], or NULL for 2^(-8(h+1)/Hq) */
   float rel_scale;           /* REL_POS constant c */
+  float softcap;             /* SOFTCAP cap (> 0, finite) */
 } attn_score_params_t;
 
 /* Block-sparse mask over q_block x kv_block blocks of the Sq x Skv grid (the

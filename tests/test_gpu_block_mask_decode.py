@@ -111,18 +111,18 @@ def small_decode_inputs(lengths, hq=8, hkv=2, max_pages=80, seed=0, poison=False
     return inp
 
 
-def run_decode(inp, score="none", label="", seqs=None, window=0):
+def run_decode(inp, score="none", label="", seqs=None, window=0, softcap=1.5, scale=None):
     dev = torch.device("cuda")
     q = inp["q"]
-    scale = 1.0 / math.sqrt(q.shape[-1])
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
     mask = "sliding" if window else "none"
     announce(f"paged decode {label} {score} window={window}")
     out, lse = af.attn_paged_decode(q.to(dev), inp["k_cache"].to(dev), inp["v_cache"].to(dev),
                                     inp["page_table"].to(dev), inp["seq_lens"].to(dev),
                                     scale=scale, mask=mask, window=window, score=score,
-                                    rel_scale=-0.01)
+                                    rel_scale=-0.01, softcap=softcap)
     torch.cuda.synchronize()
-    ss = oracle.ScoreSpec(workloads.SCORE_NAMES[score], rel_scale=-0.01)
+    ss = oracle.ScoreSpec(workloads.SCORE_NAMES[score], rel_scale=-0.01, softcap=softcap)
     ms = oracle.MaskSpec(workloads.MASK_NAMES[mask], window=window)
     o_ref, l_ref = oracle.paged_decode_ref(f64(q), f64(inp["k_cache"]), f64(inp["v_cache"]),
                                            inp["page_table"].numpy(), inp["seq_lens"].numpy(),
@@ -138,9 +138,19 @@ def run_decode(inp, score="none", label="", seqs=None, window=0):
 LENGTHS = [1, 15, 16, 17, 1023, 1024, 1025, 1280]
 
 
-@pytest.mark.parametrize("score", ["none", "alibi", "rel_pos"])
+@pytest.mark.parametrize("score", ["none", "alibi", "rel_pos", "softcap"])
 def test_paged_decode_small(score):
     run_decode(small_decode_inputs(LENGTHS, seed=1), score, "small")
+
+
+@pytest.mark.parametrize("softcap", [0.5, 8.0])
+def test_paged_decode_softcap_large_scores(softcap):
+    # scale 1 over D = 128: scores of spread ~11, saturated by the small cap
+    # and bent by cap 8 (a cap far above them would leave a softmax resting
+    # on one or two keys, where the bf16 rounding of P and O alone nears the
+    # bound)
+    run_decode(small_decode_inputs(LENGTHS, seed=4, poison=True), "softcap", "softcap",
+               window=300, softcap=softcap, scale=1.0)
 
 
 def test_paged_decode_nan_poison_and_gqa_groups():

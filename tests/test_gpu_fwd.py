@@ -21,19 +21,21 @@ from gpu_util import announce, compare, f64, requires_gpu
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
 MASKS = ["none", "causal", "sliding", "prefix_lm", "document"]
-SCORES = ["none", "alibi", "rel_pos"]
+SCORES = ["none", "alibi", "rel_pos", "softcap"]
 
 
-def oracle_specs(mask, score, window=0, prefix_len=0, doc_ids=None, rel_scale=1.0):
+def oracle_specs(mask, score, window=0, prefix_len=0, doc_ids=None, rel_scale=1.0, softcap=0.0):
     ms = oracle.MaskSpec(workloads.MASK_NAMES[mask], window=window, prefix_len=prefix_len,
                          doc_ids=None if doc_ids is None else doc_ids.cpu().numpy())
-    ss = oracle.ScoreSpec(workloads.SCORE_NAMES[score], rel_scale=rel_scale)
+    ss = oracle.ScoreSpec(workloads.SCORE_NAMES[score], rel_scale=rel_scale, softcap=softcap)
     return ms, ss
 
 
 def run_case(B, Hq, Hkv, Sq, Skv, D, dtype, mask, score, seed=0, window=100, prefix_len=70,
-             doc_lengths=(50, 130, 7, 113), rel_scale=-0.05, block_mask=False):
-    label = f"B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Skv{Skv} D{D} {dtype} {mask} {score} bm={block_mask}"
+             doc_lengths=(50, 130, 7, 113), rel_scale=-0.05, block_mask=False, softcap=1.5,
+             scale=None):
+    label = (f"B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Skv{Skv} D{D} {dtype} {mask} {score} bm={block_mask}"
+             f" scale={scale} softcap={softcap if score == 'softcap' else '-'}")
     q, k, v = workloads.randn_qkv(B, Hq, Hkv, Sq, Skv, D, dtype, seed)
     doc_ids = None
     if mask == "document":
@@ -47,16 +49,16 @@ def run_case(B, Hq, Hkv, Sq, Skv, D, dtype, mask, score, seed=0, window=100, pre
     if block_mask:
         bm = af.attn_build_block_mask(mask, B, Sq, Skv, window=window, prefix_len=prefix_len,
                                       doc_ids=dd, device=dev)
-    scale = 1.0 / math.sqrt(D)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
     announce(label)
     kw = dict(scale=scale, mask=mask, window=window, prefix_len=prefix_len, doc_ids=dd,
-              score=score, rel_scale=rel_scale, block_mask=bm)
+              score=score, rel_scale=rel_scale, softcap=softcap, block_mask=bm)
     out, lse = af.attn_fwd(qd, kd, vd, **kw)
     out32 = None
     if q.dtype == torch.bfloat16:
         out32, lse32 = af.attn_fwd(qd, kd, vd, out_dtype=torch.float32, **kw)
     torch.cuda.synchronize()
-    ms, ss = oracle_specs(mask, score, window, prefix_len, doc_ids, rel_scale)
+    ms, ss = oracle_specs(mask, score, window, prefix_len, doc_ids, rel_scale, softcap)
     o_ref, l_ref = oracle.attention_ref(f64(q), f64(k), f64(v), scale, ms, ss)
     if out32 is not None:
         # the computed values (fp32 output) at the tolerance; the bf16 output
@@ -92,8 +94,19 @@ def test_bf16_rectangular(Sq, Skv, mask):
 @pytest.mark.parametrize("D", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("mask", MASKS)
 def test_f32_small(D, mask):
-    run_case(1, 4, 2, 150, 150, D, "f32", mask, "alibi" if D == 64 else "none", seed=D,
-             doc_lengths=(40, 33, 77))
+    score = {64: "alibi", 32: "softcap", 128: "softcap"}.get(D, "none")
+    run_case(1, 4, 2, 150, 150, D, "f32", mask, score, seed=D, doc_lengths=(40, 33, 77))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("softcap", [0.3, 4.0, 12.0])
+def test_softcap_large_scores(D, softcap):
+    # scale 1: scores of spread sqrt(D) (8 or 11), far past the small caps
+    # (every score saturates towards +-cap) and bent by cap 12.  A cap far
+    # above the scores is left out here: at scale 1 the softmax then rests on
+    # one or two keys, and the bf16 rounding of P alone reaches the bound.
+    run_case(1, 4, 2, 200, 260, D, "bf16", "causal", "softcap", seed=int(softcap * 10) + D,
+             softcap=softcap, scale=1.0)
 
 
 def test_tiny_causal_f32_workload():
@@ -176,7 +189,7 @@ def sample_rows(S, rng, extra=24):
 
 
 FULL = [workloads.DENSE_BF16, workloads.CAUSAL_BF16, workloads.GQA_WINDOW_ALIBI,
-        workloads.DOCUMENT_BLOCKMASK]
+        workloads.DOCUMENT_BLOCKMASK, workloads.CAUSAL_SOFTCAP]
 
 
 @pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
@@ -193,7 +206,7 @@ def test_full_size_sampled(w):
                                       prefix_len=w.prefix_len, doc_ids=dd, device=dev)
     announce(w.name)
     kw = dict(scale=1.0 / math.sqrt(w.D), mask=w.mask, window=w.window, prefix_len=w.prefix_len,
-              doc_ids=dd, score=w.score, block_mask=bm)
+              doc_ids=dd, score=w.score, softcap=w.softcap, block_mask=bm)
     out, lse = af.attn_fwd(qd, kd, vd, **kw)
     out32, lse32 = af.attn_fwd(qd, kd, vd, out_dtype=torch.float32, **kw)
     torch.cuda.synchronize()
@@ -204,14 +217,14 @@ def test_full_size_sampled(w):
     rows = sample_rows(w.Sq, rng)
     heads = sorted({0, w.Hq - 1, w.Hq // 2 + 1})
     batches = sorted({0, w.B - 1})
-    ms, ss = oracle_specs(w.mask, w.score, w.window, w.prefix_len, doc)
+    ms, ss = oracle_specs(w.mask, w.score, w.window, w.prefix_len, doc, softcap=w.softcap)
     o_ref, l_ref = oracle.attention_ref(f64(q), f64(k), f64(v), 1.0 / math.sqrt(w.D), ms, ss,
                                         rows=rows, heads=heads, batches=batches)
     sel = np.ix_(batches, heads, rows)
     compare(f64(out32)[sel], f64(lse32)[sel], o_ref, l_ref, q.dtype, w.name + " fp32-out")
     compare(f64(out)[sel], f64(lse)[sel], o_ref, l_ref, q.dtype, w.name + " bf16-out",
             out_rounding=True)
-    if w.score == "none":
+    if w.score in ("none", "softcap"):
         # Without a bias no output row concentrates on one or two keys except
         # the first rows of causal-type masks, so |O| < 4 and the bf16 output
         # also meets the bound; those first rows are checked for every head.

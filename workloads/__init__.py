@@ -29,7 +29,7 @@ import numpy as np
 import torch
 
 MASK_NAMES = {"none": 0, "causal": 1, "sliding": 2, "prefix_lm": 3, "document": 4}
-SCORE_NAMES = {"none": 0, "alibi": 1, "rel_pos": 2}
+SCORE_NAMES = {"none": 0, "alibi": 1, "rel_pos": 2, "softcap": 3}
 
 
 @dataclass(frozen=True)
@@ -46,6 +46,7 @@ class PrefillWorkload:
     score: str = "none"
     window: int = 0
     prefix_len: int = 0
+    softcap: float = 0.0    # score "softcap": the cap
     docs: bool = False      # document ids drawn with doc_lengths()
     block_mask: bool = False
     seed: int = 0
@@ -77,9 +78,15 @@ GQA_WINDOW_ALIBI = PrefillWorkload("gqa_window1024_alibi_bf16_b2hq32hkv8s8192d12
 DOCUMENT_BLOCKMASK = PrefillWorkload("document_blockmask_bf16_b1h16s16384d128", "bf16",
                                      1, 16, 16, 16384, 16384, 128, mask="document", docs=True,
                                      block_mask=True)
+# The causal shape again with soft-capping; N(0, 1) inputs give scaled scores
+# of unit spread, so a cap of 5 bends their tails as larger caps do on
+# trained logits.
+CAUSAL_SOFTCAP = PrefillWorkload("causal_softcap5_bf16_b4h16s2048d64", "bf16", 4, 16, 16, 2048, 2048,
+                                 64, mask="causal", score="softcap", softcap=5.0)
 PAGED_DECODE = DecodeWorkload("paged_decode_bf16_n64hq32hkv8d128p16", 64, 32, 8, 128)
 
-PREFILL_WORKLOADS = [TINY_CAUSAL_F32, DENSE_BF16, CAUSAL_BF16, GQA_WINDOW_ALIBI, DOCUMENT_BLOCKMASK]
+PREFILL_WORKLOADS = [TINY_CAUSAL_F32, DENSE_BF16, CAUSAL_BF16, GQA_WINDOW_ALIBI, DOCUMENT_BLOCKMASK,
+                     CAUSAL_SOFTCAP]
 
 
 def torch_dtype(name: str):

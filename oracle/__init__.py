@@ -22,7 +22,8 @@ are lost, so each reading taken is stated where it is used):
   ``score_mod(score, b, h, q_idx, kv_idx)`` applied before softmax, and the
   five-deep loop that defines it); §全注意力 (identity score_mod);
   §相对位置编码 (bias from the query-key distance, computed in-kernel);
-  §Soft-capping (named, formula lost); §Causal Mask; §Sliding Window + Causal (the most recent 1024 tokens).
+  §Soft-capping (named, formula lost); §Causal Mask; the combination
+  sliding window + document + causal in the variant list (AND of masks); §Sliding Window + Causal (the most recent 1024 tokens).
 * [Online-Softmax page] "Attention优化｜2w字原理&图解: 从Online-Softmax到
   FlashAttention V1/V2/V3", abstract: 3-pass safe softmax, 2-pass online
   softmax and 1-pass FlashAttention are forms of one result.
@@ -38,7 +39,7 @@ invariants, library cross-checks); none is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
-    MASK_NONE, MASK_CAUSAL, MASK_SLIDING, MASK_PREFIX_LM, MASK_DOCUMENT,
+    MASK_NONE, MASK_CAUSAL, MASK_SLIDING, MASK_PREFIX_LM, MASK_DOCUMENT, MASK_AND,
     SCORE_NONE, SCORE_ALIBI, SCORE_REL_POS, SCORE_SOFTCAP,
     MaskSpec, ScoreSpec,
     alibi_slopes, visible, bias, score_mod, scores_block, kv_head,

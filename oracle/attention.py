@@ -36,13 +36,17 @@ Readings taken where the pages are silent (their formulas were images):
   (§Sliding Window + Causal: the most recent 1024 tokens, with causal);
 * PrefixLM: j <= i or j < P (named only in the variant list);
 * document mask: doc[b, i] == doc[b, j] and j <= i (named only in the list);
+* AND-composition: a key is visible when every listed kind's predicate holds,
+  each with the spec's own window / prefix / document ids (the variant list
+  names the combination sliding window + document + causal; combining masks
+  is read as intersecting them, the plain reading of "+" for restrictions);
 * indices are raw row/column numbers, as in the page's score_mod loop.
 """
 
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 from typing import Optional, Tuple
 
 import numpy as np
@@ -52,6 +56,7 @@ MASK_CAUSAL = 1
 MASK_SLIDING = 2       # causal + window
 MASK_PREFIX_LM = 3
 MASK_DOCUMENT = 4      # causal within a document
+MASK_AND = 5           # conjunction of the kinds in MaskSpec.and_kinds
 
 SCORE_NONE = 0
 SCORE_ALIBI = 1
@@ -65,6 +70,7 @@ class MaskSpec:
     window: int = 0
     prefix_len: int = 0
     doc_ids: Optional[np.ndarray] = None  # int [B, S] (query and key share it)
+    and_kinds: Tuple[int, ...] = ()       # MASK_AND: the kinds intersected
 
 
 @dataclass(frozen=True)
@@ -102,6 +108,13 @@ def visible(mask: MaskSpec, b: int, i, j) -> np.ndarray:
     if kind == MASK_DOCUMENT:
         doc = np.asarray(mask.doc_ids)[b]
         return (doc[i] == doc[j]) & (j <= i)
+    if kind == MASK_AND:
+        out = np.ones((i.shape[0], j.shape[1]), dtype=bool)
+        for part in mask.and_kinds:
+            if part == MASK_AND:
+                raise ValueError("AND terms are plain kinds")
+            out &= visible(replace(mask, kind=part, and_kinds=()), b, i[:, 0], j[0, :])
+        return out
     raise ValueError(f"unknown mask kind {kind}")
 
 
@@ -302,18 +315,20 @@ def attention_bruteforce(q, k, v, scale, mask: MaskSpec = MaskSpec(),
             x = float(score.softcap) * math.tanh(x / float(score.softcap))
         return x
 
-    def is_visible(b, qi, kj):
-        if mask.kind == MASK_NONE:
+    def is_visible(b, qi, kj, kind=mask.kind):
+        if kind == MASK_NONE:
             return True
-        if mask.kind == MASK_CAUSAL:
+        if kind == MASK_CAUSAL:
             return kj <= qi
-        if mask.kind == MASK_SLIDING:
+        if kind == MASK_SLIDING:
             return 0 <= qi - kj < mask.window
-        if mask.kind == MASK_PREFIX_LM:
+        if kind == MASK_PREFIX_LM:
             return kj <= qi or kj < mask.prefix_len
-        if mask.kind == MASK_DOCUMENT:
+        if kind == MASK_DOCUMENT:
             return doc[b][qi] == doc[b][kj] and kj <= qi
-        raise ValueError(mask.kind)
+        if kind == MASK_AND:
+            return all(is_visible(b, qi, kj, part) for part in mask.and_kinds)
+        raise ValueError(kind)
 
     out = [[[[0.0] * dv for _ in range(sq)] for _ in range(hq_count)] for _ in range(bsz)]
     lse = [[[0.0] * sq for _ in range(hq_count)] for _ in range(bsz)]

@@ -24,7 +24,7 @@ from __future__ import annotations
 import numpy as np
 
 from .attention import MaskSpec, visible, MASK_NONE, MASK_CAUSAL, MASK_SLIDING, \
-    MASK_PREFIX_LM, MASK_DOCUMENT
+    MASK_PREFIX_LM, MASK_DOCUMENT, MASK_AND
 
 
 def block_mask_ref(mask: MaskSpec, batch: int, sq: int, skv: int,
@@ -53,11 +53,12 @@ def block_mask_ref(mask: MaskSpec, batch: int, sq: int, skv: int,
 
 
 def block_mask_bruteforce(kind: int, batch: int, sq: int, skv: int, q_block: int,
-                          kv_block: int, window: int = 0, prefix_len: int = 0, doc_ids=None):
+                          kv_block: int, window: int = 0, prefix_len: int = 0, doc_ids=None,
+                          and_kinds=()):
     """Element-by-element scalar form for tiny shapes (pure Python)."""
     doc = None if doc_ids is None else np.asarray(doc_ids).tolist()
 
-    def vis(b, i, j):
+    def vis(b, i, j, kind=kind):
         if kind == MASK_NONE:
             return True
         if kind == MASK_CAUSAL:
@@ -68,6 +69,8 @@ def block_mask_bruteforce(kind: int, batch: int, sq: int, skv: int, q_block: int
             return j <= i or j < prefix_len
         if kind == MASK_DOCUMENT:
             return doc[b][i] == doc[b][j] and j <= i
+        if kind == MASK_AND:
+            return all(vis(b, i, j, part) for part in and_kinds)
         raise ValueError(kind)
 
     nqb = -(-sq // q_block)

@@ -18,7 +18,7 @@ import pytest
 import oracle
 import workloads
 from oracle import MaskSpec, ScoreSpec, MASK_NONE, MASK_CAUSAL, MASK_SLIDING, MASK_PREFIX_LM, \
-    MASK_DOCUMENT, SCORE_NONE, SCORE_ALIBI, SCORE_REL_POS
+    MASK_DOCUMENT, MASK_AND, SCORE_NONE, SCORE_ALIBI, SCORE_REL_POS
 
 
 def _ids(lengths, batch=1):
@@ -33,6 +33,10 @@ CASES = [
     (MaskSpec(MASK_SLIDING, window=17), 2, 40, 40, 8, 16),
     (MaskSpec(MASK_PREFIX_LM, prefix_len=11), 1, 30, 30, 8, 8),
     (MaskSpec(MASK_DOCUMENT, doc_ids=_ids([7, 3, 12, 9, 2], 2)), 2, 33, 33, 8, 8),
+    (MaskSpec(MASK_AND, window=6, doc_ids=_ids([7, 3, 12, 9, 2], 2),
+              and_kinds=(MASK_SLIDING, MASK_DOCUMENT)), 2, 33, 33, 8, 4),
+    (MaskSpec(MASK_AND, window=11, prefix_len=9, doc_ids=_ids([20, 13], 1),
+              and_kinds=(MASK_CAUSAL, MASK_SLIDING, MASK_DOCUMENT, MASK_PREFIX_LM)), 1, 33, 33, 4, 8),
 ]
 
 
@@ -41,7 +45,7 @@ def test_block_mask_matches_scalar_scan(ci):
     mask, b, sq, skv, qb, kb = CASES[ci]
     got = oracle.block_mask_ref(mask, b, sq, skv, qb, kb)
     want = oracle.block_mask_bruteforce(mask.kind, b, sq, skv, qb, kb, mask.window, mask.prefix_len,
-                                        mask.doc_ids)
+                                        mask.doc_ids, mask.and_kinds)
     for g, w in zip(got, want):
         assert g.dtype == w.dtype and g.shape == w.shape
         assert np.array_equal(g, w)

@@ -26,13 +26,14 @@ def _all_pins():
     pins.check_window_closed_forms()
     pins.check_prefix_closed_forms()
     pins.check_document_closed_forms()
+    pins.check_and_composition()
     pins.check_alibi_closed_form()
     pins.check_alibi_closed_form(window=7)
     pins.check_rel_pos_closed_form()
     pins.check_softcap_closed_forms()
     pins.check_value_special_cases()
     pins.check_invariances()
-    for mi in range(5):
+    for mi in range(pins.N_MASKS):
         pins.check_against_torch_sdpa(pins.all_masks(24, [5, 11, 8])[mi], pins.ALL_SCORES[1], seed=mi)
 
 
@@ -91,6 +92,21 @@ def _softcap_clip(score, s, hq, hq_count, i, j):
     return _orig_score_mod(score, s, hq, hq_count, i, j)
 
 
+def _and_as_or(mask, b, i, j):
+    if mask.kind == att.MASK_AND:
+        out = np.zeros((len(np.asarray(i)), len(np.asarray(j))), dtype=bool)
+        for part in mask.and_kinds:
+            out |= _orig_visible(att.replace(mask, kind=part, and_kinds=()), b, i, j)
+        return out
+    return _orig_visible(mask, b, i, j)
+
+
+def _and_drops_last_term(mask, b, i, j):
+    if mask.kind == att.MASK_AND and len(mask.and_kinds) > 1:
+        return _orig_visible(att.replace(mask, and_kinds=mask.and_kinds[:-1]), b, i, j)
+    return _orig_visible(mask, b, i, j)
+
+
 def _wrong_head_map(hq, hq_count, hkv_count):
     return hq % hkv_count
 
@@ -129,6 +145,8 @@ MUTATIONS = {
     "softcap_no_inner_division": ("score_mod", _softcap_no_inner_division),
     "softcap_no_outer_factor": ("score_mod", _softcap_no_outer_factor),
     "softcap_hard_clip": ("score_mod", _softcap_clip),
+    "and_as_or": ("visible", _and_as_or),
+    "and_drops_last_term": ("visible", _and_drops_last_term),
 }
 
 

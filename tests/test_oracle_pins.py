@@ -19,7 +19,7 @@ import oracle
 from oracle import attention as att
 from oracle import (MaskSpec, ScoreSpec, MASK_NONE, MASK_CAUSAL, MASK_SLIDING,
                     MASK_PREFIX_LM, MASK_DOCUMENT, SCORE_NONE, SCORE_ALIBI, SCORE_REL_POS,
-                    SCORE_SOFTCAP)
+                    SCORE_SOFTCAP, MASK_AND)
 
 RNG = np.random.default_rng(1234)
 
@@ -40,7 +40,13 @@ def all_masks(s, lengths=None):
         MaskSpec(MASK_SLIDING, window=4),
         MaskSpec(MASK_PREFIX_LM, prefix_len=5),
         MaskSpec(MASK_DOCUMENT, doc_ids=doc_ids_for(lengths, 2)),
+        # sliding window + document + causal, intersected
+        MaskSpec(MASK_AND, window=4, doc_ids=doc_ids_for(lengths, 2),
+                 and_kinds=(MASK_SLIDING, MASK_DOCUMENT, MASK_CAUSAL)),
     ]
+
+
+N_MASKS = 6
 
 
 ALL_SCORES = [ScoreSpec(SCORE_NONE), ScoreSpec(SCORE_ALIBI), ScoreSpec(SCORE_REL_POS, rel_scale=-0.3)]
@@ -91,7 +97,7 @@ def check_bruteforce(mask, score, seed=0):
     np.testing.assert_allclose(l_ref, l_bf, rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("mi", range(5))
+@pytest.mark.parametrize("mi", range(N_MASKS))
 @pytest.mark.parametrize("si", range(4))
 def test_bruteforce_matches_vectorised(mi, si):
     check_bruteforce(all_masks(16)[mi], ALL_MODS[si], seed=10 * mi + si)
@@ -109,7 +115,7 @@ def test_bruteforce_rectangular_none_mask():
 # ----------------------------------------------------------------------------
 # 1-pass recurrence (FlashAttention form) equals the 3-pass definition
 
-@pytest.mark.parametrize("mi", range(5))
+@pytest.mark.parametrize("mi", range(N_MASKS))
 def test_one_pass_matches_three_pass(mi):
     rng = np.random.default_rng(77 + mi)
     b, hq, hkv, s, d = 2, 4, 2, 37, 8
@@ -144,7 +150,7 @@ def check_against_torch_sdpa(mask, score, seed=3):
     np.testing.assert_allclose(o_ref, o_t.numpy(), rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("mi", range(5))
+@pytest.mark.parametrize("mi", range(N_MASKS))
 def test_matches_torch_cpu_sdpa(mi):
     for score in ALL_SCORES:
         check_against_torch_sdpa(all_masks(24, [5, 11, 8])[mi], score, seed=mi)
@@ -235,6 +241,62 @@ def check_document_closed_forms():
 
 def test_document_closed_forms():
     check_document_closed_forms()
+
+
+def check_and_composition():
+    # sliding window W + document + causal: row i of a document starting at
+    # st sees keys max(st, i - W + 1) .. i, so with Q = 0 LSE = ln(count) and
+    # O = the mean of those V rows
+    rng = np.random.default_rng(17)
+    lengths = [4, 1, 9, 6, 2]
+    s, d, w = sum(lengths), 3, 3
+    k, v = rand(1, 1, s, d, rng=rng), rand(1, 1, s, d, rng=rng)
+    ids = doc_ids_for(lengths)
+    starts = np.repeat(np.cumsum([0] + lengths[:-1]), lengths)
+    i = np.arange(s)
+    first = np.maximum(starts, i - w + 1)
+    m = MaskSpec(MASK_AND, window=w, doc_ids=ids, and_kinds=(MASK_SLIDING, MASK_DOCUMENT))
+    o, lse = oracle.attention_ref(np.zeros((1, 1, s, d)), k, v, 1.0, m)
+    np.testing.assert_allclose(lse[0, 0], np.log(i - first + 1.0), atol=1e-14)
+    for r in range(s):
+        np.testing.assert_allclose(o[0, 0, r], v[0, 0, first[r]:r + 1].mean(axis=0), atol=1e-14)
+    # visible-pair count by documents: sum over a document of length n of
+    # min(r + 1, W), r = 0..n-1
+    want = sum(sum(min(r + 1, w) for r in range(n)) for n in lengths)
+    assert int(oracle.visible(m, 0, i, i).sum()) == want
+    # identities of the intersection: no term is no mask; one term is that
+    # mask; causal adds nothing to a window or a document (both imply it);
+    # the prefix adds nothing to any mask that implies causal; a window
+    # longer than every document adds nothing to the document mask; one
+    # document covering everything adds nothing to the window
+    doc = doc_ids_for([5, 8, 3, 7], 1)
+    s2 = 23
+    i2 = np.arange(s2)
+    base = dict(window=4, prefix_len=6, doc_ids=doc)
+
+    def grid(kind, kinds=()):
+        return oracle.visible(MaskSpec(kind, and_kinds=kinds, **base), 0, i2, i2)
+    assert np.array_equal(grid(MASK_AND, ()), grid(MASK_NONE))
+    for kind in (MASK_CAUSAL, MASK_SLIDING, MASK_PREFIX_LM, MASK_DOCUMENT):
+        assert np.array_equal(grid(MASK_AND, (kind,)), grid(kind))
+    assert np.array_equal(grid(MASK_AND, (MASK_CAUSAL, MASK_SLIDING)), grid(MASK_SLIDING))
+    assert np.array_equal(grid(MASK_AND, (MASK_CAUSAL, MASK_DOCUMENT)), grid(MASK_DOCUMENT))
+    assert np.array_equal(grid(MASK_AND, (MASK_CAUSAL, MASK_PREFIX_LM)), grid(MASK_CAUSAL))
+    assert np.array_equal(grid(MASK_AND, (MASK_PREFIX_LM, MASK_SLIDING)), grid(MASK_SLIDING))
+    assert np.array_equal(grid(MASK_AND, (MASK_PREFIX_LM, MASK_DOCUMENT)), grid(MASK_DOCUMENT))
+    wide = MaskSpec(MASK_AND, window=8, doc_ids=doc, and_kinds=(MASK_SLIDING, MASK_DOCUMENT))
+    assert np.array_equal(oracle.visible(wide, 0, i2, i2),
+                          oracle.visible(MaskSpec(MASK_DOCUMENT, doc_ids=doc), 0, i2, i2))
+    one = MaskSpec(MASK_AND, window=4, doc_ids=np.zeros((1, s2), int), and_kinds=(MASK_SLIDING, MASK_DOCUMENT))
+    assert np.array_equal(oracle.visible(one, 0, i2, i2), grid(MASK_SLIDING))
+    # and the window + document intersection is neither of its terms
+    both = grid(MASK_AND, (MASK_SLIDING, MASK_DOCUMENT))
+    assert not np.array_equal(both, grid(MASK_SLIDING)) and not np.array_equal(both, grid(MASK_DOCUMENT))
+    assert np.array_equal(both, grid(MASK_SLIDING) & grid(MASK_DOCUMENT))
+
+
+def test_and_composition():
+    check_and_composition()
 
 
 def _geometric(r, n):

@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libattn_fa2.so")
 
 F32, BF16 = 0, 1
 MASK_KINDS = {"none": 0, "causal": 1, "sliding": 2, "prefix_lm": 3, "document": 4}
+MASK_AND = 5   # masks joined with "&", e.g. "sliding&document&causal"
 SCORE_KINDS = {"none": 0, "alibi": 1, "rel_pos": 2, "softcap": 3}
 EXPORTED = ("attn_fwd", "attn_build_block_mask", "attn_paged_decode_workspace_size",
             "attn_paged_decode", "attn_last_error")
@@ -41,7 +42,7 @@ class AttnError(RuntimeError):
 
 class MaskParams(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("prefix_len", ctypes.c_int32),
-                ("doc_ids", ctypes.c_void_p)]
+                ("doc_ids", ctypes.c_void_p), ("and_kinds", ctypes.c_uint32)]
 
 
 class ScoreParams(ctypes.Structure):
@@ -123,11 +124,24 @@ def _need_device(*tensors):
 
 
 def _mask_params(mask: str, window: int, prefix_len: int, doc_ids: Optional[torch.Tensor]):
-    if mask not in MASK_KINDS:
-        raise ValueError(f"unknown mask kind {mask!r}")
+    kind, bits = _mask_kind(mask)
     if doc_ids is not None and doc_ids.dtype != torch.int32:
         raise ValueError("doc_ids must be int32")
-    return MASK_KINDS[mask], MaskParams(int(window), int(prefix_len), _ptr(doc_ids))
+    return kind, MaskParams(int(window), int(prefix_len), _ptr(doc_ids), bits)
+
+
+def _mask_kind(mask: str):
+    """(kind, and_kinds) of a mask name; names joined with "&" intersect."""
+    if "&" not in mask:
+        if mask not in MASK_KINDS:
+            raise ValueError(f"unknown mask kind {mask!r}")
+        return MASK_KINDS[mask], 0
+    bits = 0
+    for part in mask.split("&"):
+        if part not in MASK_KINDS:
+            raise ValueError(f"unknown mask kind {part!r} in {mask!r}")
+        bits |= 1 << MASK_KINDS[part]
+    return MASK_AND, bits
 
 
 def _score_params(score: str, alibi_slopes: Optional[torch.Tensor], rel_scale: float,
@@ -224,13 +238,12 @@ def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optio
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     sk, sp = _score_params(score, alibi_slopes, rel_scale, softcap)
-    if mask not in MASK_KINDS:
-        raise ValueError(f"unknown mask {mask!r}")
-    mp = MaskParams(int(window), 0, None)
+    mk, bits = _mask_kind(mask)
+    mp = MaskParams(int(window), 0, None, bits)
     rc = lib.attn_paged_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                page_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                                lse.data_ptr(), BF16, n, hq, hkv, d, page_size, max_pages, pages,
-                               float(scale), MASK_KINDS[mask], ctypes.byref(mp), sk,
+                               float(scale), mk, ctypes.byref(mp), sk,
                                ctypes.byref(sp), workspace.data_ptr(),
                                workspace.numel() * workspace.element_size(), _stream(q.device))
     _check("attn_paged_decode", rc)

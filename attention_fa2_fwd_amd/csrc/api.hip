@@ -20,26 +20,53 @@ int fail(int code, const char *fmt, ...) {
   return code;
 }
 
-bool valid_mask_kind(int mk) { return mk >= ATTN_MASK_NONE && mk <= ATTN_MASK_DOCUMENT; }
+bool valid_mask_kind(int mk) { return mk >= ATTN_MASK_NONE && mk <= ATTN_MASK_AND; }
+
+// The kind a set of intersected kinds (bit 1 << kind each) reduces to:
+// SLIDING and DOCUMENT both imply j <= i, so CAUSAL adds nothing to either,
+// and (j <= i or j < P) holds wherever j <= i does, so PREFIX_LM adds nothing
+// to any of CAUSAL, SLIDING, DOCUMENT.  What is left is one kind, or SLIDING
+// and DOCUMENT together.
+int reduce_and(uint32_t bits) {
+  const bool win = bits & (1u << ATTN_MASK_SLIDING);
+  const bool doc = bits & (1u << ATTN_MASK_DOCUMENT);
+  if (win && doc) return attn::kMaskDocWindow;
+  if (doc) return ATTN_MASK_DOCUMENT;
+  if (win) return ATTN_MASK_SLIDING;
+  if (bits & (1u << ATTN_MASK_CAUSAL)) return ATTN_MASK_CAUSAL;
+  if (bits & (1u << ATTN_MASK_PREFIX_LM)) return ATTN_MASK_PREFIX_LM;
+  return ATTN_MASK_NONE;
+}
 bool valid_score_kind(int sk) { return sk >= ATTN_SCORE_NONE && sk <= ATTN_SCORE_SOFTCAP; }
 
 // Shared checks of mask parameters; fills the kernel-side copy.
+// Shared checks of mask parameters; fills the kernel-side copy, with an AND
+// set reduced to the kind the kernels run.  The parameters of every kind in
+// the set are checked, also those the reduction drops.
 int check_mask(int mk, const attn_mask_params_t *mp, int Sq, int Skv, attn::MaskArgs *out) {
   if (!valid_mask_kind(mk)) return fail(ATTN_ERR_INVALID, "unknown mask kind %d", mk);
-  out->kind = mk;
+  uint32_t bits = 1u << mk;
+  if (mk == ATTN_MASK_AND) {
+    if (!mp) return fail(ATTN_ERR_INVALID, "AND mask needs mask params");
+    bits = mp->and_kinds;
+    if (bits & ~0x1Fu) return fail(ATTN_ERR_INVALID, "and_kinds 0x%x names no mask kind", bits);
+  }
+  out->kind = reduce_and(bits);
   out->window = 0;
   out->prefix_len = 0;
   out->doc_ids = nullptr;
   out->doc_stride = Skv;
-  if (mk == ATTN_MASK_SLIDING) {
+  if (bits & (1u << ATTN_MASK_SLIDING)) {
     if (!mp) return fail(ATTN_ERR_INVALID, "SLIDING mask needs mask params");
     if (mp->window < 1) return fail(ATTN_ERR_INVALID, "window must be >= 1 (got %d)", mp->window);
     out->window = mp->window;
-  } else if (mk == ATTN_MASK_PREFIX_LM) {
+  }
+  if (bits & (1u << ATTN_MASK_PREFIX_LM)) {
     if (!mp) return fail(ATTN_ERR_INVALID, "PREFIX_LM mask needs mask params");
     if (mp->prefix_len < 0) return fail(ATTN_ERR_INVALID, "prefix_len must be >= 0");
     out->prefix_len = mp->prefix_len;
-  } else if (mk == ATTN_MASK_DOCUMENT) {
+  }
+  if (bits & (1u << ATTN_MASK_DOCUMENT)) {
     if (!mp || !mp->doc_ids) return fail(ATTN_ERR_INVALID, "DOCUMENT mask needs doc_ids");
     if (Sq != Skv) return fail(ATTN_ERR_UNSUPPORTED, "DOCUMENT mask needs Sq == Skv");
     out->doc_ids = mp->doc_ids;
@@ -201,11 +228,10 @@ int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
   if (page_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports page_size == 16");
   if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports Hq/Hkv <= 16");
   attn::DecodeParams p{};
-  if (!valid_mask_kind(mk)) return fail(ATTN_ERR_INVALID, "unknown mask kind %d", mk);
-  if (mk != ATTN_MASK_NONE && mk != ATTN_MASK_SLIDING)
-    return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports mask kinds NONE and SLIDING");
   int rc = check_mask(mk, mp, 1, 1, &p.mask);
   if (rc) return rc;
+  if (p.mask.kind != ATTN_MASK_NONE && p.mask.kind != ATTN_MASK_SLIDING)
+    return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports no mask or a sliding window");
   rc = check_score(sk, sp, &p.score);
   if (rc) return rc;
   if (N == 0) {

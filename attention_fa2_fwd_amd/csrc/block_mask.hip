@@ -16,7 +16,10 @@
 // DOCUMENT decides a block from the ids' summary where it can (blocks wholly
 // above the diagonal, blocks that straddle it, id ranges that do not meet,
 // blocks holding a single id) and otherwise scans for a shared id; no
-// ordering of the ids is assumed.
+// ordering of the ids is assumed.  DOCUMENT with a window (the AND of the two)
+// takes the window's interval test first; where the window covers the whole
+// block the document test decides, and where it covers part of it a scan of
+// the pairs inside the window looks for a shared id.
 //
 // One workgroup per (batch, query block), one key block per thread; the list
 // is compacted with wave ballots, 256 key blocks at a time.
@@ -94,6 +97,35 @@ __device__ __forceinline__ void document_block(const int32_t *doc_row, const int
   }
 }
 
+// DOCUMENT and SLIDING together: a pair is visible when the ids agree and
+// 0 <= i - j < W.
+__device__ __forceinline__ void doc_window_block(const int32_t *doc_row, const int32_t *qdoc, int nq,
+                                                 int qmin, int qmax, bool q_uniform, int window,
+                                                 int q0, int q1, int k0, int k1, bool &any, bool &all) {
+  const bool w_any = (q1 - k0 >= 0) && (q0 - k1 < window);
+  const bool w_all = (q0 - k1 >= 0) && (q1 - k0 < window);
+  any = false;
+  all = false;
+  if (!w_any) return;
+  bool d_any, d_all;
+  document_block(doc_row, qdoc, nq, qmin, qmax, q_uniform, q0, q1, k0, k1, d_any, d_all);
+  if (!d_any) return;            // no pair with equal ids and j <= i at all
+  if (w_all) {                   // every pair is inside the window
+    any = true;
+    all = d_all;
+    return;
+  }
+  // The window covers part of the block: key j sees rows
+  // max(q0, j) .. min(q1, j + W - 1); look there for its id, keys nearest
+  // the diagonal first.
+  for (int j = k1; j >= k0 && !any; --j) {
+    const int d = doc_row[j];
+    const int lo = max(q0, j);
+    const int hi = min(q1, j + window - 1);
+    for (int i = lo; i <= hi && !any; ++i) any = (qdoc[i - q0] == d);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void block_mask_kernel(BMArgs a) {
   __shared__ int32_t qdoc[1024];
   __shared__ int32_t wave_cnt[kThreads / 64];
@@ -107,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(BMArgs a) {
   const int q0 = qb * a.q_block;
   const int q1 = min(a.Sq, q0 + a.q_block) - 1;
   const int nq = q1 - q0 + 1;
-  const bool doc = a.mask.kind == ATTN_MASK_DOCUMENT;
+  const bool doc = a.mask.kind == ATTN_MASK_DOCUMENT || a.mask.kind == kMaskDocWindow;
   const int32_t *doc_row = doc ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride : nullptr;
 
   const size_t row = (size_t)b * a.nqb + qb;
@@ -139,8 +171,11 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(BMArgs a) {
       const int k1 = min(a.Skv, k0 + a.kv_block) - 1;
       if (!doc)
         interval_block(a.mask, q0, q1, k0, k1, listed, full);
-      else
+      else if (a.mask.kind == ATTN_MASK_DOCUMENT)
         document_block(doc_row, qdoc, nq, qmin, qmax, q_uniform, q0, q1, k0, k1, listed, full);
+      else
+        doc_window_block(doc_row, qdoc, nq, qmin, qmax, q_uniform, a.mask.window, q0, q1, k0, k1,
+                         listed, full);
     }
 
     // Compact: rank of this thread's listed block among listed blocks.

@@ -27,7 +27,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Kernel-side copy of the mask parameters (plain values, passed by value).
+// Kernel-side mask kind for SLIDING and DOCUMENT together (what any AND set
+// holding both reduces to).  Internal only: never a value of the public enum.
+constexpr int kMaskDocWindow = 6;
+
+// Kernel-side copy of the mask parameters (plain values, passed by value);
+// kind is NONE..DOCUMENT or kMaskDocWindow.
 struct MaskArgs {
   int kind;
   int window;
@@ -55,6 +60,7 @@ __device__ __forceinline__ bool mask_visible(const MaskArgs &m, int i, int j, in
     case ATTN_MASK_SLIDING: return (j <= i) && (i - j < m.window);
     case ATTN_MASK_PREFIX_LM: return (j <= i) || (j < m.prefix_len);
     case ATTN_MASK_DOCUMENT: return (j <= i) && (doc_row[j] == doc_i);
+    case kMaskDocWindow: return (j <= i) && (i - j < m.window) && (doc_row[j] == doc_i);
     default: return false;
   }
 }

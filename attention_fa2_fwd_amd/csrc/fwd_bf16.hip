@@ -112,6 +112,10 @@ template <int D, int MASK, int MOD, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   using C = FwdCfg<D>;
   constexpr bool GEN = MOD != kModRaw;   // x materialised before the max
+  // Mask terms: document ids compared (DOCUMENT, and DOCUMENT with a window)
+  // and a window on i - j (SLIDING, and DOCUMENT with a window).
+  constexpr bool DOC = MASK == ATTN_MASK_DOCUMENT || MASK == kMaskDocWindow;
+  constexpr bool WIN = MASK == ATTN_MASK_SLIDING || MASK == kMaskDocWindow;
   // K and V double buffers as four distinct LDS objects, always addressed
   // through their own names: the compiler can then tell that reading one
   // buffer does not depend on buffer->LDS loads still in flight to another,
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     int lo = 0, hi = a.Skv;
     if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
       hi = min(a.Skv, qlast + 1);
-    } else if (MASK == ATTN_MASK_SLIDING) {
+    } else if (WIN) {
       hi = min(a.Skv, qlast + 1);
       lo = max(0, q0 - a.mask.window + 1);
     } else if (MASK == ATTN_MASK_PREFIX_LM) {
@@ -213,8 +217,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     return s_full[bi] != 0;
   };
 
-  const int32_t *doc_row = (MASK == ATTN_MASK_DOCUMENT) ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride
-                                                        : nullptr;
+  const int32_t *doc_row = DOC ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride : nullptr;
 
   // ---- HBM/L2 -> LDS through buffer_load ... lds.  Wave w, load i fills
   // row block blk = 4i + w: lane L writes bytes [16L, 16L + 16) of the block,
@@ -280,14 +283,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // Soft cap in log2 units and its exponent factor (2 / cap) * c.
   const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
   const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
-  const int doc_i = (MASK == ATTN_MASK_DOCUMENT) ? doc_row[min(qi, a.Sq - 1)] : 0;
+  const int doc_i = DOC ? doc_row[min(qi, a.Sq - 1)] : 0;
   asm volatile("" ::"v"(doc_i));   // complete the load before the tile loop
 
   // Visibility class of a key tile for this wave.
   auto tile_empty = [&](int k0) __attribute__((always_inline)) -> bool {
     bool e = (qw0 >= a.Sq) || (k0 >= a.Skv);
     if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) e = e || (k0 > qw1);
-    if (MASK == ATTN_MASK_SLIDING) e = e || (k0 > qw1) || (qw0 - (k0 + kBN - 1) >= a.mask.window);
+    if (WIN) e = e || (k0 > qw1) || (qw0 - (k0 + kBN - 1) >= a.mask.window);
     if (MASK == ATTN_MASK_PREFIX_LM) e = e || ((k0 > qw1) && (k0 >= a.mask.prefix_len));
     return e;
   };
@@ -296,6 +299,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     if (MASK == ATTN_MASK_CAUSAL) f = f && (k0 + kBN - 1 <= qw0);
     if (MASK == ATTN_MASK_DOCUMENT) f = f && (k0 + kBN - 1 <= qw0) && tile_block_full(n);
     if (MASK == ATTN_MASK_SLIDING) f = f && (k0 + kBN - 1 <= qw0) && (qw1 - k0 < a.mask.window);
+    if (MASK == kMaskDocWindow)
+      f = f && (k0 + kBN - 1 <= qw0) && (qw1 - k0 < a.mask.window) && tile_block_full(n);
     if (MASK == ATTN_MASK_PREFIX_LM) f = f && ((k0 + kBN - 1 <= qw0) || (k0 + kBN <= a.mask.prefix_len));
     return f;
   };
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
       // the raw scores too: c > 0 on that path).
       const int dq = qi - jb;                       // j <= qi  <=>  off <= dq
       int32_t kd[2][4][4];
-      if (MASK == ATTN_MASK_DOCUMENT) {
+      if (DOC) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -361,6 +366,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
           if (MASK == ATTN_MASK_SLIDING) vis = vis && (off <= dq) && (dq - off < a.mask.window);
           if (MASK == ATTN_MASK_PREFIX_LM) vis = vis && ((off <= dq) || (off < a.mask.prefix_len - jb));
           if (MASK == ATTN_MASK_DOCUMENT) vis = vis && (off <= dq) && (kd[kb][r >> 2][r & 3] == doc_i);
+          if (MASK == kMaskDocWindow)
+            vis = vis && (off <= dq) && (dq - off < a.mask.window) && (kd[kb][r >> 2][r & 3] == doc_i);
           s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
     }
@@ -455,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     load_k(k_lds0, tile_key0(0));
     load_v(v_lds0, tile_key0(0));
     if (n_tiles > 1) load_k(k_lds1, tile_key0(1));
-    if (MASK == ATTN_MASK_DOCUMENT && wave == 0) {
+    if (DOC && wave == 0) {
       kdoc[0][lane] = load_doc(tile_key0(0));
       if (n_tiles > 1) kdoc[1][lane] = load_doc(tile_key0(1));
     }
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     const int k0 = tile_key0(n);
     int doc_fill = 0;
     if (n + 2 < n_tiles) {
-      if (MASK == ATTN_MASK_DOCUMENT && wave == 0) doc_fill = load_doc(tile_key0(n + 2));
+      if (DOC && wave == 0) doc_fill = load_doc(tile_key0(n + 2));
       load_k(k_fill, tile_key0(n + 2));
     }
     if (n + 1 < n_tiles) load_v(v_fill, tile_key0(n + 1));
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     } else if (next_live) {
       compute_s(s_next, k_next);
     }
-    if (MASK == ATTN_MASK_DOCUMENT && wave == 0 && n + 2 < n_tiles) kdoc[(n + 2) % 3][lane] = doc_fill;
+    if (DOC && wave == 0 && n + 2 < n_tiles) kdoc[(n + 2) % 3][lane] = doc_fill;
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads and LDS stores are done
     __syncthreads();
   };
@@ -555,6 +562,7 @@ hipError_t launch_mask(const KernelArgs &a, int mask, unsigned grid, hipStream_t
     case ATTN_MASK_SLIDING: return launch_variant<D, ATTN_MASK_SLIDING, MOD, OUT_F32>(a, grid, stream);
     case ATTN_MASK_PREFIX_LM: return launch_variant<D, ATTN_MASK_PREFIX_LM, MOD, OUT_F32>(a, grid, stream);
     case ATTN_MASK_DOCUMENT: return launch_variant<D, ATTN_MASK_DOCUMENT, MOD, OUT_F32>(a, grid, stream);
+    case kMaskDocWindow: return launch_variant<D, kMaskDocWindow, MOD, OUT_F32>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
   const bool has_bias = a.score.kind == ATTN_SCORE_ALIBI || a.score.kind == ATTN_SCORE_REL_POS;
   const bool has_cap = a.score.kind == ATTN_SCORE_SOFTCAP;
   const float cap2 = a.score.softcap * kLog2e;   // the cap in log2 units
-  const int32_t *doc_row = (mk == ATTN_MASK_DOCUMENT) ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride
+  const bool has_doc = mk == ATTN_MASK_DOCUMENT || mk == kMaskDocWindow;
+  const int32_t *doc_row = has_doc ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride
                                                       : nullptr;
   const int doc_i = (doc_row && row_ok) ? doc_row[qi] : -1;
 
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Args a) {
     list = a.bm_idx + row * a.bm_nkb;
   } else if (mk == ATTN_MASK_CAUSAL || mk == ATTN_MASK_DOCUMENT) {
     hi0 = min(a.Skv, qlast + 1);
-  } else if (mk == ATTN_MASK_SLIDING) {
+  } else if (mk == ATTN_MASK_SLIDING || mk == kMaskDocWindow) {
     hi0 = min(a.Skv, qlast + 1);
     lo0 = max(0, q0 - a.mask.window + 1);
   } else if (mk == ATTN_MASK_PREFIX_LM) {

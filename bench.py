@@ -44,6 +44,10 @@ def visible_pairs(mask: str, S: int, window: int = 0, doc_lengths=None) -> int:
         return sum(min(i + 1, w) for i in range(S))
     if mask == "document":
         return sum(n * (n + 1) // 2 for n in doc_lengths)
+    if mask in ("sliding&document", "sliding&document&causal"):
+        w = window
+        return sum(n * (n + 1) // 2 if n <= w else w * (w + 1) // 2 + (n - w) * w
+                   for n in doc_lengths)
     raise ValueError(mask)
 
 
@@ -196,8 +200,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="run one workload (dense, causal, gqa, document, causal_softcap, decode, "
-                         "decode_window) and exit")
+                    help="run one workload (dense, causal, gqa, document, causal_softcap, "
+                         "document_window, decode, decode_window) and exit")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy, to calibrate byte counters")
     args = ap.parse_args()
@@ -230,7 +234,8 @@ def main():
     if args.only:
         sel = {"dense": workloads.DENSE_BF16, "causal": workloads.CAUSAL_BF16,
                "gqa": workloads.GQA_WINDOW_ALIBI, "document": workloads.DOCUMENT_BLOCKMASK,
-               "causal_softcap": workloads.CAUSAL_SOFTCAP}
+               "causal_softcap": workloads.CAUSAL_SOFTCAP,
+               "document_window": workloads.DOC_WINDOW_BLOCKMASK}
         if args.only == "decode":
             r = bench_decode(af, torch, workloads, args.steps, args.warmup)
         elif args.only == "decode_window":
@@ -322,7 +327,8 @@ def main():
         extra = {}
         for name, w in (("gqa_window1024_alibi", workloads.GQA_WINDOW_ALIBI),
                         ("document_blockmask", workloads.DOCUMENT_BLOCKMASK),
-                        ("causal_softcap5", workloads.CAUSAL_SOFTCAP)):
+                        ("causal_softcap5", workloads.CAUSAL_SOFTCAP),
+                        ("document_window1024_blockmask", workloads.DOC_WINDOW_BLOCKMASK)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             extra[name] = bench_prefill(af, torch, workloads, w, 20, 3)
         print("[bench] paged decode", file=sys.stderr, flush=True)

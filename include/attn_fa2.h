@@ -56,19 +56,30 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
  *   CAUSAL    j <= i
  *   SLIDING   0 <= i - j < window            (causal + window of `window` keys, self included)
  *   PREFIX_LM j <= i  or  j < prefix_len
- *   DOCUMENT  doc_ids[b, i] == doc_ids[b, j]  and  j <= i                      */
+ *   DOCUMENT  doc_ids[b, i] == doc_ids[b, j]  and  j <= i
+ *   AND       every kind k with bit (1u << k) set in and_kinds holds, each with
+ *             the same params (the variant list's combination "sliding
+ *             window + document + causal" is and_kinds = SLIDING | DOCUMENT |
+ *             CAUSAL bits); no bit set means no mask.  Bits other than those
+ *             of NONE..DOCUMENT are an error.  The set is reduced exactly
+ *             before launch: CAUSAL adds nothing to SLIDING or DOCUMENT (both
+ *             imply j <= i), PREFIX_LM adds nothing to a kind that implies
+ *             j <= i, so every set is one of the kinds above or SLIDING and
+ *             DOCUMENT together.                                              */
 typedef enum {
   ATTN_MASK_NONE = 0,
   ATTN_MASK_CAUSAL = 1,
   ATTN_MASK_SLIDING = 2,
   ATTN_MASK_PREFIX_LM = 3,
-  ATTN_MASK_DOCUMENT = 4
+  ATTN_MASK_DOCUMENT = 4,
+  ATTN_MASK_AND = 5
 } attn_mask_kind_t;
 
 typedef struct {
   int32_t window;          /* SLIDING: number of keys, >= 1 */
   int32_t prefix_len;      /* PREFIX_LM: bidirectional prefix length, >= 0 */
   const int32_t *doc_ids;  /* DOCUMENT: device int32 [B, S] (Sq == Skv == S) */
+  uint32_t and_kinds;      /* AND: bit (1u << kind) per intersected kind */
 } attn_mask_params_t;
 
 /* Score modifiers, applied to the scaled score x = scale * q.k before the

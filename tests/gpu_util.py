@@ -63,3 +63,20 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label="", out_rounding=False)
     assert summary["o_mean"] <= tol["o_mean"], f"{label}: {summary}"
     assert summary["lse_max"] <= tol["lse"], f"{label}: {summary}"
     return summary
+
+
+def mask_spec(mask: str, window=0, prefix_len=0, doc_ids=None):
+    """The oracle's MaskSpec for a mask name of the binding ("&" joins the
+    kinds of an intersection)."""
+    import oracle
+    import workloads
+    doc = None if doc_ids is None else (doc_ids.cpu().numpy() if hasattr(doc_ids, "cpu") else doc_ids)
+    if "&" in mask:
+        kinds = tuple(workloads.MASK_NAMES[p] for p in mask.split("&"))
+        return oracle.MaskSpec(oracle.MASK_AND, window=window, prefix_len=prefix_len, doc_ids=doc,
+                               and_kinds=kinds)
+    return oracle.MaskSpec(workloads.MASK_NAMES[mask], window=window, prefix_len=prefix_len, doc_ids=doc)
+
+
+def has_document(mask: str) -> bool:
+    return "document" in mask.split("&")

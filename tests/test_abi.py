@@ -32,8 +32,8 @@ def test_exports_every_declared_symbol():
 
 
 def _fwd(lib, dt=1, out_dt=None, B=1, Hq=4, Hkv=2, Sq=16, Skv=16, D=64, scale=0.125, mk=0, window=0,
-         prefix=0, sk=0, bm=None, null_score=False, softcap=0.0):
-    mp = af.MaskParams(window, prefix, None)
+         prefix=0, sk=0, bm=None, null_score=False, softcap=0.0, and_kinds=0):
+    mp = af.MaskParams(window, prefix, None, and_kinds)
     sp = af.ScoreParams(None, 1.0, softcap)
     out_dt = dt if out_dt is None else out_dt
     return lib.attn_fwd(None, None, None, None, None, dt, out_dt, B, Hq, Hkv, Sq, Skv, D, scale, mk,
@@ -62,6 +62,12 @@ def _fwd(lib, dt=1, out_dt=None, B=1, Hq=4, Hkv=2, Sq=16, Skv=16, D=64, scale=0.
     (dict(sk=3, softcap=float("inf")), -1),
     (dict(sk=3, softcap=float("nan")), -1),
     (dict(sk=3, softcap=30.0), -1),     # valid cap, null tensors
+    (dict(mk=5, and_kinds=1 << 5), -1),           # AND names no kind
+    (dict(mk=5, and_kinds=1 << 2), -1),           # AND with a window of 0
+    (dict(mk=5, and_kinds=(1 << 2) | (1 << 4), window=8), -1),   # no doc_ids
+    (dict(mk=5, and_kinds=(1 << 3), prefix=-2), -1),
+    (dict(mk=5, and_kinds=0), -1),                # empty AND is no mask; null tensors
+    (dict(mk=5, and_kinds=(1 << 1) | (1 << 2) | (1 << 3), window=8), -1),   # null tensors
     (dict(scale=float("nan")), -1),
     (dict(), -1),                       # valid shapes but null tensors
 ])
@@ -107,8 +113,8 @@ def test_block_mask_builder_checks():
 
 
 def _dec(lib, N=2, Hq=8, Hkv=2, D=128, page=16, max_pages=4, pool=8, dt=1, mk=0, window=0, sk=0,
-         ws=None, ws_bytes=0, softcap=0.0):
-    mp = af.MaskParams(window, 0, None)
+         ws=None, ws_bytes=0, softcap=0.0, and_kinds=0, doc=None):
+    mp = af.MaskParams(window, 0, doc, and_kinds)
     sp = af.ScoreParams(None, 1.0, softcap)
     return lib.attn_paged_decode(None, None, None, None, None, None, None, dt, N, Hq, Hkv, D, page,
                                  max_pages, pool, 0.1, mk, ctypes.byref(mp), sk, ctypes.byref(sp), ws,
@@ -124,6 +130,9 @@ def test_paged_decode_checks():
     assert _dec(lib, Hq=34, Hkv=2) == -2
     assert _dec(lib, mk=1) == -2                           # only NONE and SLIDING
     assert _dec(lib, sk=3) == -1                           # SOFTCAP needs a cap > 0
+    assert _dec(lib, mk=5, and_kinds=(1 << 1) | (1 << 2), window=9) == -1   # a window: null tensors
+    assert _dec(lib, mk=5, and_kinds=1 << 1) == -2                          # causal alone
+    assert _dec(lib, mk=5, and_kinds=1 << 4, doc=8) == -2                   # a document mask
     assert _dec(lib, mk=9) == -1
     assert _dec(lib, mk=2, window=0) == -1                 # window must be >= 1
     assert _dec(lib, mk=2, window=100) == -1               # valid mask, null tensors

@@ -11,7 +11,7 @@ import torch
 import attention_fa2_fwd_amd as af
 import oracle
 import workloads
-from gpu_util import announce, compare, f64, requires_gpu
+from gpu_util import announce, compare, f64, has_document, mask_spec, requires_gpu
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -36,6 +36,17 @@ BM_CASES = [
     ("document", 1, 513, 513, 32, 128, dict(random_ids=40)),
     ("document", 1, 600, 600, 128, 128, dict(pattern=[(0, 100), (1, 50), (0, 80), (2, 200), (1, 170)])),
     ("document", 1, 257, 257, 128, 128, dict(lengths=[257])),     # one id; a 1-row last block
+    # window + document (+ causal): interval test, document summary, and the
+    # scan of the pairs inside a window that covers part of a block
+    ("sliding&document", 2, 1000, 1000, 128, 128, dict(window=100, lengths=[300, 1, 129, 127, 443])),
+    ("sliding&document&causal", 1, 999, 999, 48, 80, dict(window=37, lengths=[10, 500, 489])),
+    ("sliding&document", 2, 700, 700, 64, 64, dict(window=50, random_ids=4)),
+    ("sliding&document", 1, 513, 513, 32, 128, dict(window=200, random_ids=40)),
+    ("sliding&document&causal", 1, 600, 600, 128, 128,
+     dict(window=130, pattern=[(0, 100), (1, 50), (0, 80), (2, 200), (1, 170)])),
+    ("sliding&document", 1, 4096, 4096, 128, 128, dict(window=1, lengths=[1000, 3000, 96])),
+    ("sliding&document", 1, 4096, 4096, 128, 128, dict(window=5000, lengths=[1000, 3000, 96])),
+    ("causal&prefix_lm&sliding", 1, 777, 777, 128, 128, dict(window=300, prefix_len=500)),
 ]
 
 
@@ -55,20 +66,35 @@ def test_block_mask_bit_exact(case):
     mask, B, Sq, Skv, qb, kb, kw = BM_CASES[case]
     dev = torch.device("cuda")
     doc = None
-    if mask == "document":
+    if has_document(mask):
         doc = torch.from_numpy(_case_doc_ids(B, Sq, kw))
     announce(f"block mask {BM_CASES[case][:6]}")
     bm = af.attn_build_block_mask(mask, B, Sq, Skv, q_block=qb, kv_block=kb,
                                   window=kw.get("window", 0), prefix_len=kw.get("prefix_len", 0),
                                   doc_ids=doc.to(dev) if doc is not None else None, device=dev)
     torch.cuda.synchronize()
-    ms = oracle.MaskSpec(workloads.MASK_NAMES[mask], window=kw.get("window", 0),
-                         prefix_len=kw.get("prefix_len", 0),
-                         doc_ids=None if doc is None else doc.numpy())
+    ms = mask_spec(mask, kw.get("window", 0), kw.get("prefix_len", 0), doc)
     num, idx, full = oracle.block_mask_ref(ms, B, Sq, Skv, qb, kb)
     assert np.array_equal(bm.kv_num_blocks.cpu().numpy(), num)
     assert np.array_equal(bm.kv_indices.cpu().numpy(), idx)
     assert np.array_equal(bm.kv_full.cpu().numpy(), full)
+
+
+def test_block_mask_document_window_workload():
+    w = workloads.DOC_WINDOW_BLOCKMASK
+    dev = torch.device("cuda")
+    lengths = workloads.doc_lengths(w.Sq, seed=w.seed)
+    doc = torch.from_numpy(_ids(lengths, w.B))
+    announce("block mask document + window workload")
+    bm = af.attn_build_block_mask(w.mask, w.B, w.Sq, w.Skv, window=w.window, doc_ids=doc.to(dev),
+                                  device=dev)
+    torch.cuda.synchronize()
+    num, idx, full = oracle.block_mask_ref(mask_spec(w.mask, w.window, doc_ids=doc), w.B, w.Sq, w.Skv,
+                                           128, 128)
+    assert np.array_equal(bm.kv_num_blocks.cpu().numpy(), num)
+    assert np.array_equal(bm.kv_indices.cpu().numpy(), idx)
+    assert np.array_equal(bm.kv_full.cpu().numpy(), full)
+    assert int(num.sum()) == 890 and int(full.sum()) == 594
 
 
 def test_block_mask_document_workload():

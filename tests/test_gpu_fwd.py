@@ -16,7 +16,7 @@ import torch
 import attention_fa2_fwd_amd as af
 import oracle
 import workloads
-from gpu_util import announce, compare, f64, requires_gpu
+from gpu_util import announce, compare, f64, has_document, mask_spec, requires_gpu
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -25,8 +25,7 @@ SCORES = ["none", "alibi", "rel_pos", "softcap"]
 
 
 def oracle_specs(mask, score, window=0, prefix_len=0, doc_ids=None, rel_scale=1.0, softcap=0.0):
-    ms = oracle.MaskSpec(workloads.MASK_NAMES[mask], window=window, prefix_len=prefix_len,
-                         doc_ids=None if doc_ids is None else doc_ids.cpu().numpy())
+    ms = mask_spec(mask, window, prefix_len, doc_ids)
     ss = oracle.ScoreSpec(workloads.SCORE_NAMES[score], rel_scale=rel_scale, softcap=softcap)
     return ms, ss
 
@@ -38,7 +37,7 @@ def run_case(B, Hq, Hkv, Sq, Skv, D, dtype, mask, score, seed=0, window=100, pre
              f" scale={scale} softcap={softcap if score == 'softcap' else '-'}")
     q, k, v = workloads.randn_qkv(B, Hq, Hkv, Sq, Skv, D, dtype, seed)
     doc_ids = None
-    if mask == "document":
+    if has_document(mask):
         lens = list(doc_lengths)
         lens[-1] += Sq - sum(lens)
         doc_ids = torch.from_numpy(workloads.doc_ids_from_lengths(lens, B))
@@ -109,12 +108,38 @@ def test_softcap_large_scores(D, softcap):
              softcap=softcap, scale=1.0)
 
 
+# Intersections of masks: window + document is the one that needs its own
+# kernel variant; the others reduce to a single kind before launch.
+AND_MASKS = ["sliding&document", "sliding&document&causal", "causal&prefix_lm", "prefix_lm&sliding",
+             "document&prefix_lm&causal", "causal&sliding"]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", AND_MASKS)
+@pytest.mark.parametrize("score", ["none", "alibi", "softcap"])
+def test_bf16_and_masks(D, mask, score):
+    run_case(2, 4, 2, 300, 300, D, "bf16", mask, score, seed=D + len(mask) + len(score), window=37)
+
+
+@pytest.mark.parametrize("window", [1, 16, 64, 65, 127, 128, 129, 200, 1000])
+@pytest.mark.parametrize("block_mask", [False, True])
+def test_bf16_document_window_sizes(window, block_mask):
+    run_case(1, 4, 4, 700, 700, 128, "bf16", "sliding&document&causal", "none", seed=window,
+             window=window, doc_lengths=(300, 41, 129, 1, 229), block_mask=block_mask)
+
+
+@pytest.mark.parametrize("mask", AND_MASKS)
+def test_f32_and_masks(mask):
+    run_case(1, 4, 2, 150, 150, 64, "f32", mask, "alibi", seed=len(mask), window=21,
+             doc_lengths=(40, 33, 77))
+
+
 def test_tiny_causal_f32_workload():
     w = workloads.TINY_CAUSAL_F32
     run_case(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.dtype, w.mask, w.score, seed=w.seed)
 
 
-@pytest.mark.parametrize("mask", ["causal", "sliding", "prefix_lm", "document"])
+@pytest.mark.parametrize("mask", ["causal", "sliding", "prefix_lm", "document", "sliding&document&causal"])
 def test_block_mask_path_equals_dense_path(mask):
     """The BlockMask-driven kernel matches the oracle and, bit for bit, the
     analytic-range kernel (the same tiles hold the same visible keys)."""
@@ -189,7 +214,7 @@ def sample_rows(S, rng, extra=24):
 
 
 FULL = [workloads.DENSE_BF16, workloads.CAUSAL_BF16, workloads.GQA_WINDOW_ALIBI,
-        workloads.DOCUMENT_BLOCKMASK, workloads.CAUSAL_SOFTCAP]
+        workloads.DOCUMENT_BLOCKMASK, workloads.CAUSAL_SOFTCAP, workloads.DOC_WINDOW_BLOCKMASK]
 
 
 @pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])

@@ -78,6 +78,11 @@ GQA_WINDOW_ALIBI = PrefillWorkload("gqa_window1024_alibi_bf16_b2hq32hkv8s8192d12
 DOCUMENT_BLOCKMASK = PrefillWorkload("document_blockmask_bf16_b1h16s16384d128", "bf16",
                                      1, 16, 16, 16384, 16384, 128, mask="document", docs=True,
                                      block_mask=True)
+# The pages' combination sliding window + document + causal, intersected,
+# on the document workload's shape and documents.
+DOC_WINDOW_BLOCKMASK = PrefillWorkload("document_window1024_blockmask_bf16_b1h16s16384d128", "bf16",
+                                       1, 16, 16, 16384, 16384, 128, mask="sliding&document&causal",
+                                       window=1024, docs=True, block_mask=True)
 # The causal shape again with soft-capping; N(0, 1) inputs give scaled scores
 # of unit spread, so a cap of 5 bends their tails as larger caps do on
 # trained logits.
@@ -86,7 +91,7 @@ CAUSAL_SOFTCAP = PrefillWorkload("causal_softcap5_bf16_b4h16s2048d64", "bf16", 4
 PAGED_DECODE = DecodeWorkload("paged_decode_bf16_n64hq32hkv8d128p16", 64, 32, 8, 128)
 
 PREFILL_WORKLOADS = [TINY_CAUSAL_F32, DENSE_BF16, CAUSAL_BF16, GQA_WINDOW_ALIBI, DOCUMENT_BLOCKMASK,
-                     CAUSAL_SOFTCAP]
+                     CAUSAL_SOFTCAP, DOC_WINDOW_BLOCKMASK]
 
 
 def torch_dtype(name: str):

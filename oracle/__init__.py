@@ -23,7 +23,9 @@ are lost, so each reading taken is stated where it is used):
   five-deep loop that defines it); §全注意力 (identity score_mod);
   §相对位置编码 (bias from the query-key distance, computed in-kernel);
   §Soft-capping (named, formula lost); §Causal Mask; the combination
-  sliding window + document + causal in the variant list (AND of masks); §Sliding Window + Causal (the most recent 1024 tokens).
+  sliding window + document + causal in the variant list (AND of masks);
+  the backward by automatic differentiation (intro) and its deterministic,
+  recomputing algorithm (§性能); §Sliding Window + Causal (the most recent 1024 tokens).
 * [Online-Softmax page] "Attention优化｜2w字原理&图解: 从Online-Softmax到
   FlashAttention V1/V2/V3", abstract: 3-pass safe softmax, 2-pass online
   softmax and 1-pass FlashAttention are forms of one result.
@@ -47,6 +49,7 @@ from .attention import (  # noqa: F401
     attention_rows, attention_ref, attention_bruteforce, attention_one_pass,
 )
 from .block_mask import block_mask_ref, block_mask_bruteforce  # noqa: F401
+from .backward import attention_backward_ref, attention_backward_rows, softmax_row_dot_ref  # noqa: F401
 from .paged_decode import (  # noqa: F401
     gather_paged_kv, paged_decode_ref, split_partials_ref, lse_combine_ref,
 )

@@ -31,7 +31,7 @@ MASK_KINDS = {"none": 0, "causal": 1, "sliding": 2, "prefix_lm": 3, "document": 
 MASK_AND = 5   # masks joined with "&", e.g. "sliding&document&causal"
 SCORE_KINDS = {"none": 0, "alibi": 1, "rel_pos": 2, "softcap": 3}
 EXPORTED = ("attn_fwd", "attn_build_block_mask", "attn_paged_decode_workspace_size",
-            "attn_paged_decode", "attn_last_error")
+            "attn_paged_decode", "attn_bwd_workspace_size", "attn_bwd", "attn_last_error")
 
 
 class AttnError(RuntimeError):
@@ -97,6 +97,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       i32, i32, f32, i32, ctypes.POINTER(MaskParams), i32,
                                       ctypes.POINTER(ScoreParams), vp, ctypes.c_size_t, vp]
     lib.attn_paged_decode.restype = i32
+    lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                             f32, i32, ctypes.POINTER(MaskParams), i32, ctypes.POINTER(ScoreParams),
+                             vp, ctypes.c_size_t, vp]
+    lib.attn_bwd.restype = i32
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -248,3 +254,38 @@ def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optio
                                workspace.numel() * workspace.element_size(), _stream(q.device))
     _check("attn_paged_decode", rc)
     return out, lse
+
+
+def attn_bwd(q, k, v, out, lse, dout, *, scale: Optional[float] = None, mask: str = "none",
+             window: int = 0, prefix_len: int = 0, doc_ids=None, score: str = "none",
+             alibi_slopes=None, rel_scale: float = 1.0, softcap: float = 0.0, workspace=None,
+             dq=None, dk=None, dv=None):
+    """Gradients of attn_fwd from its output and LSE.  q, out, dout
+    [B,Hq,Sq,D] and k, v [B,Hkv,Skv,D] bf16; lse [B,Hq,Sq] float32.  Returns
+    (dq, dk, dv) float32.  The mask and score arguments are the forward's."""
+    lib = load_library()
+    for t in (q, k, v, out, dout):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("attn_bwd takes bf16 q, k, v, out, dout")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    b, hq, sq, d = q.shape
+    hkv, skv = k.shape[1], k.shape[2]
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    need = int(lib.attn_bwd_workspace_size(b, hq, sq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need_device(q, k, v, out, lse, dout, dq, dk, dv, workspace, doc_ids, alibi_slopes)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mk, mp = _mask_params(mask, window, prefix_len, doc_ids)
+    sk, sp = _score_params(score, alibi_slopes, rel_scale, softcap)
+    rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), BF16, b, hq, hkv,
+                      sq, skv, d, float(scale), mk, ctypes.byref(mp), sk, ctypes.byref(sp),
+                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                      _stream(q.device))
+    _check("attn_bwd", rc)
+    return dq, dk, dv

@@ -267,4 +267,62 @@ int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
   return launch_result(attn::launch_paged_decode(p, (hipStream_t)stream), "attn_paged_decode");
 }
 
+size_t attn_bwd_workspace_size(int B, int Hq, int Sq) {
+  if (B <= 0 || Hq <= 0 || Sq <= 0) return 0;
+  return ((size_t)B * Hq * Sq * sizeof(float) + 255) / 256 * 256;
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
+             const void *dout, float *dq, float *dk, float *dv, attn_dtype_t dt, int B, int Hq, int Hkv,
+             int Sq, int Skv, int D, float scale, attn_mask_kind_t mk, const attn_mask_params_t *mp,
+             attn_score_kind_t sk, const attn_score_params_t *sp, void *workspace,
+             size_t workspace_bytes, void *stream) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || D <= 0)
+    return fail(ATTN_ERR_INVALID, "negative size (B=%d Hq=%d Hkv=%d Sq=%d Skv=%d D=%d)", B, Hq,
+                Hkv, Sq, Skv, D);
+  if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0))
+    return fail(ATTN_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  if (dt != ATTN_BF16 && dt != ATTN_F32) return fail(ATTN_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the backward supports bf16 inputs only");
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "the backward supports D in {64, 128} (got %d)", D);
+  if ((int64_t)Skv * D * 2 > 2147483647LL || (int64_t)Sq * D * 2 > 2147483647LL)
+    return fail(ATTN_ERR_UNSUPPORTED, "the backward needs Sq, Skv * D * 2 < 2^31 bytes per head");
+  attn::BwdParams p{};
+  int rc = check_mask(mk, mp, Sq, Skv, &p.mask);
+  if (rc) return rc;
+  rc = check_score(sk, sp, &p.score);
+  if (rc) return rc;
+  if (!(scale == scale)) return fail(ATTN_ERR_INVALID, "scale is NaN");
+  if (B == 0 || Hq == 0 || (Sq == 0 && Skv == 0)) {
+    g_err[0] = '\0';
+    return ATTN_OK;
+  }
+  const size_t need = attn_bwd_workspace_size(B, Hq, Sq);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (((uintptr_t)workspace) % 256 != 0) return fail(ATTN_ERR_INVALID, "workspace must be 256-byte aligned");
+  if ((Sq > 0 && (!q || !out || !lse || !dout || !dq)) || (Skv > 0 && (!k || !v || !dk || !dv)))
+    return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  const double grid = (double)B * Hq * ((Sq + 127) / 128) + (double)B * Hkv * ((Skv + 127) / 128);
+  if (grid > 2147483647.0) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.row_dot = (float *)workspace;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Skv = Skv;
+  p.D = D;
+  p.scale = scale;
+  return launch_result(attn::launch_bwd_bf16(p, (hipStream_t)stream), "attn_bwd");
+}
+
 }  // extern "C"

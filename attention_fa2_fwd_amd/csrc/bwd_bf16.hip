@@ -1,0 +1,665 @@
+// Attention backward from the stored LSE, bf16 inputs, fp32 gradients, MFMA
+// on gfx950 (CDNA4).
+//
+// The FlexAttention write-up ("新PyTorch API：几行代码实现不同注意力变体，兼具
+// FlashAttention性能和PyTorch灵活性") produces its backward by automatic
+// differentiation of the forward (introduction) and describes it as
+// deterministic, recomputing more intermediates than FlashAttention-2
+// (§性能).  This backward follows that description: no atomics, every
+// gradient element written by one workgroup, and P recomputed from the
+// forward's LSE wherever it is needed.  With x = s Q K^T, S = score_mod(x)
+// masked, P = softmax(S) = exp(S - LSE):
+//
+//   D_i = sum_d dO_id O_id                       (bwd_row_dot_kernel)
+//   dP  = dO V^T,  dS = P (dP - D),  dX = dS score_mod'(x)
+//   dQ  = s dX K                                 (bwd_dq_kernel)
+//   dV  = P^T dO,  dK = s dX^T Q                 (bwd_dkdv_kernel)
+//
+// The two main kernels reuse the forward kernel's MFMA conventions
+// (v_mfma_f32_32x32x16_bf16, 4 waves x 32 rows, LDS tiles of 1 KiB row
+// blocks filled by buffer_load ... lds and read either row-wise or through
+// the transposing ds_read_b64_tr_b16):
+//  * bwd_dq_kernel, one workgroup per (b, hq, 128 query rows), streams 64-key
+//    tiles of K and V.  S^T = K Q^T and dP^T = V dO^T take K and V rows from
+//    LDS as the A operand and Q^T, dO^T from registers as the B operand; the
+//    lane then holds one query and 16 keys, so LSE and D are one register
+//    each, and dS^T leaves the accumulator already in the B-operand layout of
+//    dQ^T += K^T dS^T, whose A operand is the transposed read of the K tile.
+//  * bwd_dkdv_kernel, one workgroup per (b, hkv, 128 keys), streams 32-row
+//    tiles of Q and dO for every query head of the GQA group, so dK and dV
+//    sum the group in registers.  S = Q K^T and dP = dO V^T take Q and dO
+//    rows from LDS and K, V (kept in registers) as the B operand; the lane
+//    then holds one key, P and dS are already the B operands of
+//    dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed
+//    from the same LDS tiles.  Per-query LSE and D are staged in LDS with the
+//    tile.
+// Tiles without a visible pair are skipped and the predicate is dropped on
+// tiles where every pair is visible, from the mask's closed-form bounds.
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr int kThreads = 256;
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kPad = 64;           // bytes between LDS row blocks
+constexpr int kQRows = 128;        // query rows per dQ workgroup
+constexpr int kKTile = 64;         // key rows per tile in the dQ kernel
+constexpr int kKRows = 128;        // keys per dK/dV workgroup
+constexpr int kQTile = 32;         // query rows per tile in the dK/dV kernel
+// Score forms: additive (raw scores or a bias) or the soft cap.
+constexpr int kModAdd = 0, kModCap = 1;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS tile of ROWS rows of D bf16: row t lives in 1 KiB block t % NB at slot
+// t / NB, blocks padded apart.
+template <int D, int ROWS>
+struct Tile {
+  static constexpr int ROWB = D * 2;
+  static constexpr int NB = ROWS * ROWB / 1024;
+  static constexpr int BLK = 1024 + kPad;
+  static constexpr int BYTES = NB * BLK;
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int LOADS = NB / 4;              // direct loads per wave per tile
+  static_assert(NB % 4 == 0 && 32 % NB == 0 && (NB <= 8 || NB == 16), "row block mapping");
+  static constexpr int off(int t) { return (t % NB) * BLK + (t / NB) * ROWB; }
+};
+
+struct BwdArgs {
+  const __bf16 *q, *k, *v, *dout;
+  const float *lse, *row_dot;
+  float *dq, *dk, *dv;
+  int B, Hq, Hkv, Sq, Skv;
+  float scale, scale_log2;
+  MaskArgs mask;
+  ScoreArgs score;
+};
+
+__device__ __forceinline__ s16x4 lds_read_tr(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+}
+
+// visible(i, j) of the mask kind, given the two document ids when the kind
+// compares them.
+template <int MASK>
+__device__ __forceinline__ bool pair_visible(const MaskArgs &m, int i, int j, int doc_i, int doc_j) {
+  if (MASK == ATTN_MASK_NONE) return true;
+  if (MASK == ATTN_MASK_CAUSAL) return j <= i;
+  if (MASK == ATTN_MASK_SLIDING) return (j <= i) && (i - j < m.window);
+  if (MASK == ATTN_MASK_PREFIX_LM) return (j <= i) || (j < m.prefix_len);
+  if (MASK == ATTN_MASK_DOCUMENT) return (j <= i) && (doc_i == doc_j);
+  if (MASK == kMaskDocWindow) return (j <= i) && (i - j < m.window) && (doc_i == doc_j);
+  return false;
+}
+
+// Visibility class of the block of queries [i0, i1] x keys [j0, j1]:
+// no visible pair (empty) or every pair visible (full), from the mask's
+// bounds.  Document masks are never full here (no id summaries).
+template <int MASK>
+__device__ __forceinline__ bool block_empty(const MaskArgs &m, int i0, int i1, int j0, int j1) {
+  if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) return j0 > i1;
+  if (MASK == ATTN_MASK_SLIDING || MASK == kMaskDocWindow) return (j0 > i1) || (i0 - j1 >= m.window);
+  if (MASK == ATTN_MASK_PREFIX_LM) return (j0 > i1) && (j0 >= m.prefix_len);
+  return false;
+}
+template <int MASK>
+__device__ __forceinline__ bool block_full(const MaskArgs &m, int i0, int i1, int j0, int j1) {
+  if (MASK == ATTN_MASK_NONE) return true;
+  if (MASK == ATTN_MASK_CAUSAL) return j1 <= i0;
+  if (MASK == ATTN_MASK_SLIDING) return (j1 <= i0) && (i1 - j0 < m.window);
+  if (MASK == ATTN_MASK_PREFIX_LM) return (j1 <= i0) || (j1 < m.prefix_len);
+  return false;
+}
+
+// Log2-domain modified score of raw dot product s for query i, key j, and
+// the factor score_mod'(x) of the chain rule.
+template <int MOD>
+__device__ __forceinline__ float mod_score(float s, float c_log2, float bias2, float cap_k, float cap2,
+                                           int i, int j) {
+  if (MOD == kModCap) return softcap_log2_fast(s, cap_k, cap2);
+  return __builtin_fmaf(s, c_log2, bias2 * (float)(j - i));
+}
+template <int MOD>
+__device__ __forceinline__ float mod_grad(float x, float inv_cap2) {
+  if (MOD == kModCap) {
+    const float t = x * inv_cap2;   // tanh of the scaled score
+    return __builtin_fmaf(-t, t, 1.0f);
+  }
+  return 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_d dO_id O_id, one row per CPR lanes (CPR = D / 8 divides 64).
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_row_dot_kernel(const __bf16 *o, const __bf16 *dout,
+                                                                float *row_dot, long rows) {
+  constexpr int CPR = D / 8;
+  const long t = (long)blockIdx.x * kThreads + threadIdx.x;
+  const long row = t / CPR;
+  const int c = (int)(t % CPR);
+  float acc = 0.0f;
+  if (row < rows) {
+    const bf16x8 x = *(const bf16x8 *)(o + row * D + 8 * c);
+    const bf16x8 g = *(const bf16x8 *)(dout + row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int w = CPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
+  if (row < rows && c == 0) row_dot[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (b, hq, 128 query rows); wave w owns rows
+// q0 + 32w .. + 31, lane (h, l32) the query q0 + 32w + l32.
+template <int D, int MASK, int MOD>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+  using T = Tile<D, kKTile>;
+  constexpr int NDC = D / 16, NDB = D / 32;
+  constexpr bool DOC = MASK == ATTN_MASK_DOCUMENT || MASK == kMaskDocWindow;
+  constexpr bool WIN = MASK == ATTN_MASK_SLIDING || MASK == kMaskDocWindow;
+  __shared__ __align__(16) char k_lds0[T::BYTES];
+  __shared__ __align__(16) char k_lds1[T::BYTES];
+  __shared__ __align__(16) char v_lds0[T::BYTES];
+  __shared__ __align__(16) char v_lds1[T::BYTES];
+  __shared__ __align__(16) int32_t kdoc0[kKTile];
+  __shared__ __align__(16) int32_t kdoc1[kKTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int n_qtiles = (a.Sq + kQRows - 1) / kQRows;
+  const int bh_count = a.B * a.Hq;
+  const int qt = n_qtiles - 1 - (int)(blockIdx.x / bh_count);   // longest key ranges first
+  const int bh = (int)(blockIdx.x % bh_count);
+  const int b = bh / a.Hq;
+  const int hq = bh - b * a.Hq;
+  const int hkv = (hq * a.Hkv) / a.Hq;
+  const int q0 = qt * kQRows;
+  const int qw0 = q0 + wave * 32;
+  const int qw1 = min(qw0 + 31, a.Sq - 1);
+  const int qi = qw0 + l32;
+  const int qr = min(qi, a.Sq - 1);
+
+  const size_t q_base = ((size_t)(b * a.Hq + hq) * a.Sq) * D;
+  const size_t kv_base = ((size_t)(b * a.Hkv + hkv) * a.Skv) * D;
+
+  // Q^T and dO^T fragments (B operands): lane holds X[qi][16c + 8h .. + 7].
+  bf16x8 qf[NDC], df[NDC];
+  {
+    const bf16x8 *qs = (const bf16x8 *)(a.q + q_base + (size_t)qr * D);
+    const bf16x8 *ds = (const bf16x8 *)(a.dout + q_base + (size_t)qr * D);
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+      qf[c] = qs[2 * c + h];
+      df[c] = ds[2 * c + h];
+    }
+  }
+  const size_t row = (size_t)(b * a.Hq + hq) * a.Sq + qr;
+  const float lse2 = a.lse[row] * kLog2e;
+  const float dsum = a.row_dot[row];
+  const float c_log2 = a.scale_log2;
+  const float bias2 = (MOD == kModAdd) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
+  const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
+  const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
+  const float inv_cap2 = (MOD == kModCap) ? 1.0f / cap2 : 0.0f;
+  const int32_t *doc_row = DOC ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride : nullptr;
+  const int doc_i = DOC ? doc_row[qr] : 0;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+
+  // Key tiles of the workgroup's rows.
+  const int qlast = min(q0 + kQRows, a.Sq) - 1;
+  int lo = 0, hi = a.Skv;
+  if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
+    hi = min(a.Skv, qlast + 1);
+  } else if (WIN) {
+    hi = min(a.Skv, qlast + 1);
+    lo = max(0, q0 - a.mask.window + 1);
+  } else if (MASK == ATTN_MASK_PREFIX_LM) {
+    hi = min(a.Skv, max(qlast + 1, a.mask.prefix_len));
+  }
+  const int t_first = lo / kKTile;
+  const int n_tiles = (hi > lo) ? (hi + kKTile - 1) / kKTile - t_first : 0;
+
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.k + kv_base), (short)0, a.Skv * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.v + kv_base), (short)0, a.Skv * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t d_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(doc_row ? doc_row : a.mask.doc_ids), (short)0, doc_row ? a.Skv * 4 : 0, kBufferFlags);
+  // Load i of wave w fills row block 4i + w: lane L writes its 16 bytes at
+  // slot L / CPR, chunk L % CPR (row (4i + w) + NB * (L / CPR)).
+  const int ld_off = ((wave + T::NB * (lane / T::CPR)) * D + (lane % T::CPR) * 8) * 2;
+  auto load_tile = [&](char *dst, __amdgpu_buffer_rsrc_t rs, int row0) __attribute__((always_inline)) {
+    const int soff = __builtin_amdgcn_readfirstlane(row0 * D * 2);
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (4 * i + wave) * T::BLK), 16,
+                                               ld_off + i * (4 * D * 2), soff, 0, 0);
+  };
+  auto load_doc = [&](int key0) __attribute__((always_inline)) -> int {
+    return __builtin_amdgcn_raw_buffer_load_b32(d_rsrc, lane * 4, __builtin_amdgcn_readfirstlane(key0 * 4), 0);
+  };
+
+  // Row reads (A operand, rows 32 kb + l32, d chunk 16c + 8h) and transposed
+  // reads (A operand K^T: lane groups of 4 point at 4 consecutive d of key
+  // 4h + (lane & 15) / 4 of each 8-key half chunk).
+  const int rd_row = T::off(l32) + h * 16;
+  const int tr_j = lane & 15;
+  const int rd_tr = T::off(4 * h + (tr_j >> 2)) + (16 * ((lane >> 4) & 1) + 4 * (tr_j & 3)) * 2;
+
+  auto tile_step = [&](int k0, const char *kt, const char *vt, const int32_t *kdoc) __attribute__((always_inline)) {
+    if (block_empty<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1) || qw0 >= a.Sq) return;
+    const bool full = block_full<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1) && (k0 + kKTile <= a.Skv);
+    // S^T and dP^T for the two 32-key blocks.
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) {
+        const int o = rd_row + T::off(32 * kb) + 32 * c;
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(kt + o), qf[c], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(vt + o), df[c], dp[kb], 0, 0, 0);
+      }
+    }
+    // dS^T element r of block kb: key j = k0 + 32 kb + 8 (r / 4) + 4h + r % 4.
+    const int jb = k0 + 4 * h;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+        const int j = jb + off;
+        const float x = mod_score<MOD>(s[kb][r], c_log2, bias2, cap_k, cap2, qi, j);
+        float p = fast_exp2(x - lse2);
+        if (!full) {
+          const int doc_j = DOC ? kdoc[4 * h + off] : 0;
+          const bool vis = (j < a.Skv) && pair_visible<MASK>(a.mask, qi, j, doc_i, doc_j);
+          p = vis ? p : 0.0f;
+        }
+        s[kb][r] = p * (dp[kb][r] - dsum) * mod_grad<MOD>(x, inv_cap2);
+      }
+    // dQ^T += K^T dS^T, 16 keys at a time.
+    const char *kbase = kt + rd_tr;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int kb = c >> 1;
+      const int r0 = 8 * (c & 1);
+      const u32x4 pw = {pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]), pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]),
+                        pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]), pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7])};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const s16x4 lo4 = lds_read_tr(kbase + T::off(16 * c) + 64 * db);
+        const s16x4 hi4 = lds_read_tr(kbase + T::off(16 * c + 8) + 64 * db);
+        const u32x4 kw = {__builtin_bit_cast(u32x2, lo4)[0], __builtin_bit_cast(u32x2, lo4)[1],
+                          __builtin_bit_cast(u32x2, hi4)[0], __builtin_bit_cast(u32x2, hi4)[1]};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kw), pb, acc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // Double-buffered tile loop: iteration n loads tile n + 1 into the buffers
+  // tile n - 1 used, computes tile n, then waits for its loads and meets
+  // the other waves at the barrier.
+  if (n_tiles > 0) {
+    load_tile(k_lds0, k_rsrc, t_first * kKTile);
+    load_tile(v_lds0, v_rsrc, t_first * kKTile);
+    if (DOC && wave == 0) kdoc0[lane] = load_doc(t_first * kKTile);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  auto iteration = [&](int n, char *k_cur, char *v_cur, int32_t *d_cur, char *k_nxt, char *v_nxt,
+                       int32_t *d_nxt) __attribute__((always_inline)) {
+    const int k0 = (t_first + n) * kKTile;
+    int doc_fill = 0;
+    if (n + 1 < n_tiles) {
+      load_tile(k_nxt, k_rsrc, k0 + kKTile);
+      load_tile(v_nxt, v_rsrc, k0 + kKTile);
+      if (DOC && wave == 0) doc_fill = load_doc(k0 + kKTile);
+    }
+    tile_step(k0, k_cur, v_cur, d_cur);
+    if (DOC && wave == 0 && n + 1 < n_tiles) d_nxt[lane] = doc_fill;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  int n = 0;
+  for (; n + 1 < n_tiles; n += 2) {
+    iteration(n, k_lds0, v_lds0, kdoc0, k_lds1, v_lds1, kdoc1);
+    iteration(n + 1, k_lds1, v_lds1, kdoc1, k_lds0, v_lds0, kdoc0);
+  }
+  if (n < n_tiles) iteration(n, k_lds0, v_lds0, kdoc0, k_lds1, v_lds1, kdoc1);
+
+  // dQ = s dX K: lane holds dQ^T[32 db + 8 g + 4h + e][qi].
+  if (qi < a.Sq) {
+    float *orow = a.dq + q_base + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 w = {acc[db][4 * g + 0] * a.scale, acc[db][4 * g + 1] * a.scale,
+                         acc[db][4 * g + 2] * a.scale, acc[db][4 * g + 3] * a.scale};
+        *(f32x4 *)(orow + 32 * db + 8 * g + 4 * h) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (b, hkv, 128 keys); wave w owns keys
+// j0 + 32w .. + 31, lane (h, l32) the key j0 + 32w + l32.
+template <int D, int MASK, int MOD>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  using T = Tile<D, kQTile>;
+  constexpr int NDC = D / 16, NDB = D / 32;
+  constexpr bool DOC = MASK == ATTN_MASK_DOCUMENT || MASK == kMaskDocWindow;
+  constexpr bool WIN = MASK == ATTN_MASK_SLIDING || MASK == kMaskDocWindow;
+  __shared__ __align__(16) char q_lds0[T::BYTES];
+  __shared__ __align__(16) char q_lds1[T::BYTES];
+  __shared__ __align__(16) char o_lds0[T::BYTES];   // dO tiles
+  __shared__ __align__(16) char o_lds1[T::BYTES];
+  // Per-query values of the staged tile: LSE (log2 units), D, document id.
+  __shared__ __align__(16) float qv_lse0[kQTile], qv_lse1[kQTile];
+  __shared__ __align__(16) float qv_dot0[kQTile], qv_dot1[kQTile];
+  __shared__ __align__(16) int32_t qv_doc0[kQTile], qv_doc1[kQTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int bh_count = a.B * a.Hkv;
+  const int kt = (int)(blockIdx.x / bh_count);   // first key tiles (most query tiles) first
+  const int bh = (int)(blockIdx.x % bh_count);
+  const int b = bh / a.Hkv;
+  const int hkv = bh - b * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int j0 = kt * kKRows;
+  const int jw0 = j0 + wave * 32;
+  const int jw1 = jw0 + 31;
+  const int kj = jw0 + l32;
+  const int kr = min(kj, a.Skv - 1);
+  const int jlast = min(j0 + kKRows, a.Skv) - 1;
+
+  const size_t kv_base = ((size_t)(b * a.Hkv + hkv) * a.Skv) * D;
+  // K and V rows as B operands: lane holds X[kj][16c + 8h .. + 7].
+  bf16x8 kf[NDC], vf[NDC];
+  {
+    const bf16x8 *ks = (const bf16x8 *)(a.k + kv_base + (size_t)kr * D);
+    const bf16x8 *vs = (const bf16x8 *)(a.v + kv_base + (size_t)kr * D);
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+      kf[c] = ks[2 * c + h];
+      vf[c] = vs[2 * c + h];
+    }
+  }
+  const float c_log2 = a.scale_log2;
+  const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
+  const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
+  const float inv_cap2 = (MOD == kModCap) ? 1.0f / cap2 : 0.0f;
+  const int32_t *doc_row = DOC ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride : nullptr;
+  const int doc_j = DOC ? doc_row[kr] : 0;
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  // Query tiles that may see the workgroup's keys [j0, jlast].
+  int lo = 0, hi = a.Sq - 1;
+  if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
+    lo = j0;
+  } else if (WIN) {
+    lo = j0;
+    hi = min(a.Sq - 1, jlast + a.mask.window - 1);
+  } else if (MASK == ATTN_MASK_PREFIX_LM) {
+    lo = (j0 < a.mask.prefix_len) ? 0 : j0;
+  }
+  const int t_first = lo / kQTile;
+  const int n_qt = (hi >= lo) ? hi / kQTile + 1 - t_first : 0;
+  const int n_iter = n_qt * G;   // (query head, query tile) pairs
+
+  // Loads of a (head, tile) pair: Q and dO rows into LDS by buffer_load ...
+  // lds (rows past Sq read as zero), the per-query values by wave 0.
+  const int ld_off = ((wave + T::NB * (lane / T::CPR)) * D + (lane % T::CPR) * 8) * 2;
+  auto head_of = [&](int it) __attribute__((always_inline)) { return hkv * G + it / n_qt; };
+  auto tile_q0 = [&](int it) __attribute__((always_inline)) { return (t_first + it % n_qt) * kQTile; };
+  auto load_tiles = [&](int it, char *qd, char *od) __attribute__((always_inline)) {
+    const int hq = head_of(it);
+    const size_t base = ((size_t)(b * a.Hq + hq) * a.Sq) * D;
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.q + base), (short)0, a.Sq * D * 2, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.dout + base), (short)0, a.Sq * D * 2, kBufferFlags);
+    const int soff = __builtin_amdgcn_readfirstlane(tile_q0(it) * D * 2);
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)(qd + (4 * i + wave) * T::BLK), 16,
+                                               ld_off + i * (4 * D * 2), soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(orr, (lds_void *)(od + (4 * i + wave) * T::BLK), 16,
+                                               ld_off + i * (4 * D * 2), soff, 0, 0);
+    }
+  };
+  // Per-query values for lane < 32 of wave 0: LSE in log2 units (+inf past
+  // Sq, so p = 0 there), D, document id.
+  struct QVals {
+    float lse2, dot;
+    int doc;
+  };
+  auto fetch_qvals = [&](int it) __attribute__((always_inline)) -> QVals {
+    const int i = tile_q0(it) + lane;
+    QVals r{INFINITY, 0.0f, -1};
+    if (lane < kQTile && i < a.Sq) {
+      const size_t row = (size_t)(b * a.Hq + head_of(it)) * a.Sq + i;
+      r.lse2 = a.lse[row] * kLog2e;
+      r.dot = a.row_dot[row];
+      if (DOC) r.doc = doc_row[i];
+    }
+    return r;
+  };
+  auto store_qvals = [&](const QVals &r, float *ls, float *dt, int32_t *dc) __attribute__((always_inline)) {
+    if (lane < kQTile) {
+      ls[lane] = r.lse2;
+      dt[lane] = r.dot;
+      if (DOC) dc[lane] = r.doc;
+    }
+  };
+
+  const int rd_row = T::off(l32) + h * 16;
+  const int tr_j = lane & 15;
+  const int rd_tr = T::off(4 * h + (tr_j >> 2)) + (16 * ((lane >> 4) & 1) + 4 * (tr_j & 3)) * 2;
+
+  auto tile_step = [&](int it, const char *qt_, const char *ot, const float *ls, const float *dt,
+                       const int32_t *dc) __attribute__((always_inline)) {
+    const int i0 = tile_q0(it);
+    const int i1 = i0 + kQTile - 1;
+    if (jw0 >= a.Skv || block_empty<MASK>(a.mask, i0, i1, jw0, jw1)) return;
+    const bool full = block_full<MASK>(a.mask, i0, i1, jw0, jw1);
+    const int hq = head_of(it);
+    const float bias2 = (MOD == kModAdd) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
+    // S = Q K^T and dP = dO V^T for the 32 queries: element r is query
+    // i0 + 8 (r / 4) + 4h + r % 4, key kj.
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+      const int o = rd_row + 32 * c;
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(qt_ + o), kf[c], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(ot + o), vf[c], dp, 0, 0, 0);
+    }
+    float p[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qo = 8 * g + 4 * h;   // query offset of elements 4g .. 4g + 3
+      const f32x4 l4 = *(const f32x4 *)(ls + qo);
+      const f32x4 d4 = *(const f32x4 *)(dt + qo);
+      int4 c4 = int4{0, 0, 0, 0};
+      if (DOC && !full) c4 = *(const int4 *)(dc + qo);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        const int i = i0 + qo + e;
+        const float x = mod_score<MOD>(s[r], c_log2, bias2, cap_k, cap2, i, kj);
+        float pr = fast_exp2(x - l4[e]);
+        if (!full) {
+          const int doc_i = (e == 0) ? c4.x : (e == 1) ? c4.y : (e == 2) ? c4.z : c4.w;
+          pr = pair_visible<MASK>(a.mask, i, kj, doc_i, doc_j) ? pr : 0.0f;
+        }
+        p[r] = pr;
+        s[r] = pr * (dp[r] - d4[e]) * mod_grad<MOD>(x, inv_cap2);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time.
+    const char *obase = ot + rd_tr;
+    const char *qbase = qt_ + rd_tr;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r0 = 8 * c;
+      const u32x4 pw = {pack_bf16x2(p[r0 + 0], p[r0 + 1]), pack_bf16x2(p[r0 + 2], p[r0 + 3]),
+                        pack_bf16x2(p[r0 + 4], p[r0 + 5]), pack_bf16x2(p[r0 + 6], p[r0 + 7])};
+      const u32x4 sw = {pack_bf16x2(s[r0 + 0], s[r0 + 1]), pack_bf16x2(s[r0 + 2], s[r0 + 3]),
+                        pack_bf16x2(s[r0 + 4], s[r0 + 5]), pack_bf16x2(s[r0 + 6], s[r0 + 7])};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+      const bf16x8 sb = __builtin_bit_cast(bf16x8, sw);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const s16x4 olo = lds_read_tr(obase + T::off(16 * c) + 64 * db);
+        const s16x4 ohi = lds_read_tr(obase + T::off(16 * c + 8) + 64 * db);
+        const u32x4 ow = {__builtin_bit_cast(u32x2, olo)[0], __builtin_bit_cast(u32x2, olo)[1],
+                          __builtin_bit_cast(u32x2, ohi)[0], __builtin_bit_cast(u32x2, ohi)[1]};
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ow), pb, dv[db], 0, 0, 0);
+        const s16x4 qlo = lds_read_tr(qbase + T::off(16 * c) + 64 * db);
+        const s16x4 qhi = lds_read_tr(qbase + T::off(16 * c + 8) + 64 * db);
+        const u32x4 qw = {__builtin_bit_cast(u32x2, qlo)[0], __builtin_bit_cast(u32x2, qlo)[1],
+                          __builtin_bit_cast(u32x2, qhi)[0], __builtin_bit_cast(u32x2, qhi)[1]};
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qw), sb, dk[db], 0, 0, 0);
+      }
+    }
+  };
+
+  if (n_iter > 0) {
+    load_tiles(0, q_lds0, o_lds0);
+    if (wave == 0) store_qvals(fetch_qvals(0), qv_lse0, qv_dot0, qv_doc0);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  auto iteration = [&](int it, char *q_cur, char *o_cur, float *l_cur, float *d_cur, int32_t *c_cur,
+                       char *q_nxt, char *o_nxt, float *l_nxt, float *d_nxt, int32_t *c_nxt)
+      __attribute__((always_inline)) {
+    QVals nv{INFINITY, 0.0f, -1};
+    if (it + 1 < n_iter) {
+      load_tiles(it + 1, q_nxt, o_nxt);
+      if (wave == 0) nv = fetch_qvals(it + 1);
+    }
+    tile_step(it, q_cur, o_cur, l_cur, d_cur, c_cur);
+    if (wave == 0 && it + 1 < n_iter) store_qvals(nv, l_nxt, d_nxt, c_nxt);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it + 1 < n_iter; it += 2) {
+    iteration(it, q_lds0, o_lds0, qv_lse0, qv_dot0, qv_doc0, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1);
+    iteration(it + 1, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1, q_lds0, o_lds0, qv_lse0, qv_dot0, qv_doc0);
+  }
+  if (it < n_iter)
+    iteration(it, q_lds0, o_lds0, qv_lse0, qv_dot0, qv_doc0, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1);
+
+  // dK = s dX^T Q, dV = P^T dO: lane holds X^T[32 db + 8 g + 4h + e][kj].
+  if (kj < a.Skv) {
+    float *krow = a.dk + kv_base + (size_t)kj * D;
+    float *vrow = a.dv + kv_base + (size_t)kj * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 wk = {dk[db][4 * g + 0] * a.scale, dk[db][4 * g + 1] * a.scale,
+                          dk[db][4 * g + 2] * a.scale, dk[db][4 * g + 3] * a.scale};
+        const f32x4 wv = {dv[db][4 * g + 0], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+        *(f32x4 *)(krow + 32 * db + 8 * g + 4 * h) = wk;
+        *(f32x4 *)(vrow + 32 * db + 8 * g + 4 * h) = wv;
+      }
+  }
+}
+
+template <int D, int MASK, int MOD>
+hipError_t launch_main(const BwdArgs &a, hipStream_t stream) {
+  const unsigned grid_q = (unsigned)(((a.Sq + kQRows - 1) / kQRows) * a.B * a.Hq);
+  if (grid_q > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD>), dim3(grid_q), dim3(kThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const unsigned grid_k = (unsigned)(((a.Skv + kKRows - 1) / kKRows) * a.B * a.Hkv);
+  if (grid_k > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, MOD>), dim3(grid_k), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <int D, int MOD>
+hipError_t launch_mask(const BwdArgs &a, hipStream_t stream) {
+  switch (a.mask.kind) {
+    case ATTN_MASK_NONE: return launch_main<D, ATTN_MASK_NONE, MOD>(a, stream);
+    case ATTN_MASK_CAUSAL: return launch_main<D, ATTN_MASK_CAUSAL, MOD>(a, stream);
+    case ATTN_MASK_SLIDING: return launch_main<D, ATTN_MASK_SLIDING, MOD>(a, stream);
+    case ATTN_MASK_PREFIX_LM: return launch_main<D, ATTN_MASK_PREFIX_LM, MOD>(a, stream);
+    case ATTN_MASK_DOCUMENT: return launch_main<D, ATTN_MASK_DOCUMENT, MOD>(a, stream);
+    case kMaskDocWindow: return launch_main<D, kMaskDocWindow, MOD>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const BwdParams &p, hipStream_t stream) {
+  BwdArgs a;
+  a.q = (const __bf16 *)p.q;
+  a.k = (const __bf16 *)p.k;
+  a.v = (const __bf16 *)p.v;
+  a.dout = (const __bf16 *)p.dout;
+  a.lse = p.lse;
+  a.row_dot = p.row_dot;
+  a.dq = p.dq;
+  a.dk = p.dk;
+  a.dv = p.dv;
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.Sq = p.Sq;
+  a.Skv = p.Skv;
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * kLog2e;
+  a.mask = p.mask;
+  a.score = p.score;
+  const long rows = (long)p.B * p.Hq * p.Sq;
+  if (rows > 0) {
+    const long threads = rows * (D / 8);
+    hipLaunchKernelGGL(bwd_row_dot_kernel<D>, dim3((unsigned)((threads + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, (const __bf16 *)p.out, a.dout, p.row_dot, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.score.kind == ATTN_SCORE_SOFTCAP) return launch_mask<D, kModCap>(a, stream);
+  return launch_mask<D, kModAdd>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t stream) {
+  if (p.D == 64) return launch_d<64>(p, stream);
+  if (p.D == 128) return launch_d<128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -24,6 +24,19 @@ struct FwdParams {
 
 // bf16 MFMA path, D in {64, 128}.
 hipError_t launch_fwd_bf16(const FwdParams &p, hipStream_t stream);
+
+struct BwdParams {
+  const void *q, *k, *v, *out, *dout;   // bf16
+  const float *lse;
+  float *dq, *dk, *dv;
+  float *row_dot;   // workspace [B, Hq, Sq]: sum_d dO * O
+  int B, Hq, Hkv, Sq, Skv, D;
+  float scale;
+  MaskArgs mask;
+  ScoreArgs score;
+};
+// Backward from the stored LSE, bf16 inputs, fp32 gradients, D in {64, 128}.
+hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t stream);
 // fp32 path, D in {16, 32, 64, 128, 256}.
 hipError_t launch_fwd_f32(const FwdParams &p, hipStream_t stream);
 

@@ -161,6 +161,36 @@ int attn_build_block_mask(attn_mask_kind_t mk, const attn_mask_params_t *mp, int
                           int Skv, int q_block, int kv_block, int32_t *kv_num_blocks,
                           int32_t *kv_indices, uint8_t *kv_full, void *stream);
 
+/* attn_bwd_workspace_size — bytes of device scratch attn_bwd needs: one
+ * float per query row, B * Hq * Sq * 4, rounded up to 256.                  */
+size_t attn_bwd_workspace_size(int B, int Hq, int Sq);
+
+/* attn_bwd — gradients of attn_fwd from its stored LSE.  The FlexAttention
+ * write-up obtains its backward by automatic differentiation of the forward
+ * (introduction) and runs a deterministic algorithm that recomputes more
+ * than FlashAttention-2 (§性能); this one writes every gradient element from
+ * one workgroup, without atomics, and recomputes P = exp(S - LSE).
+ * With x = scale * q.k, S = score_mod(x) masked and P = softmax(S):
+ *   dV = P^T dO,  dS = P (dO V^T - rowsum(dO * O)),
+ *   dQ = scale * (dS score_mod'(x)) K,  dK = scale * (dS score_mod'(x))^T Q,
+ * and a kv head's dK, dV sum every query head of its group.
+ *   q, out, dout [B, Hq, Sq, D]; k, v [B, Hkv, Skv, D]       bf16, device
+ *   lse          [B, Hq, Sq] float32: the forward's LSE (natural log)
+ *   dq           [B, Hq, Sq, D]   float32 (written)
+ *   dk, dv       [B, Hkv, Skv, D] float32 (written; zeros for keys no query sees)
+ *   scale, mk/mp, sk/sp: those of the forward call (same meaning and checks)
+ *   workspace: device scratch of at least attn_bwd_workspace_size(B, Hq, Sq)
+ *   bytes, 256-byte aligned; caller-owned, contents on entry do not matter.
+ * A row with no visible key contributes nothing.  Supported: dt = BF16,
+ * D in {64, 128} (others return -2).  No BlockMask argument: tiles are
+ * skipped from each mask's closed-form bounds, document ids are compared
+ * per element.  Errors as attn_fwd, plus -4 for a short workspace.         */
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
+             const void *dout, float *dq, float *dk, float *dv, attn_dtype_t dt, int B, int Hq, int Hkv,
+             int Sq, int Skv, int D, float scale, attn_mask_kind_t mk, const attn_mask_params_t *mp,
+             attn_score_kind_t sk, const attn_score_params_t *sp, void *workspace,
+             size_t workspace_bytes, void *stream);
+
 /* attn_paged_decode_workspace_size — bytes of device scratch attn_paged_decode
  * needs for this shape: fp32 partial outputs and log-sum-exps of every key
  * split, for splits as small as 16 pages (the launch takes 64-page splits,

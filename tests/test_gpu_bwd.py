@@ -1,0 +1,149 @@
+"""GPU parity of attn_bwd against the CPU float64 oracle, through the C ABI.
+
+The backward takes the forward's bf16 output O and float32 LSE from attn_fwd
+on the same inputs (the way a caller uses it) and a seeded dO; the oracle
+differentiates its own forward from q, k, v, dO alone.  Every gradient
+element is compared, on shapes that span several 128-row query tiles,
+64-key tiles and 32-query tiles with ragged tails, every mask kind and score
+modifier, both head dims and GQA; the causal B=4 H=16 S=2048 D=64 shape the
+bench times is checked on whole heads.
+
+Tolerance (bf16 inputs, fp32 gradients).  Each gradient is a sum of
+products in which one factor, P (for dV) or dS (for dK, dQ), is rounded to
+bf16 first: relative error at most 2^-9 per term, so the sum's relative
+error is at most 2^-9 when its terms share a sign and about 2^-9 / sqrt(3)
+when their signs are random; the row term D, formed from the bf16 output O,
+adds a like amount to dS.  Each gradient tensor G is held to
+    mean |G - G_ref| <= 2^-8 * max(mean |G_ref|, FLOOR)
+    max  |G - G_ref| <= 1e-2 * max(max |G_ref|, FLOOR)
+(the forward's max-abs bound, relative), with FLOOR = 1/16 for tensors whose
+exact value is zero (one key: P = 1, dS = 0, dQ = 0).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_fa2_fwd_amd as af
+import oracle
+import workloads
+from gpu_util import announce, f64, has_document, mask_spec, requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+BWD_MAX_REL = 1.0e-2
+BWD_MEAN_REL = 2.0 ** -8
+FLOOR = 1.0 / 16
+
+MASKS = ["none", "causal", "sliding", "prefix_lm", "document", "sliding&document&causal"]
+SCORES = ["none", "alibi", "rel_pos", "softcap"]
+
+
+def compare_grads(got, ref, label):
+    summary = {}
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = f64(g)
+        assert g.shape == r.shape, (name, g.shape, r.shape)
+        assert np.all(np.isfinite(g)), f"{label} {name}: non-finite"
+        err = np.abs(g - r)
+        scale_max = max(np.abs(r).max(), FLOOR)
+        scale_mean = max(np.abs(r).mean(), FLOOR)
+        summary[name] = (float(err.max() / scale_max), float(err.mean() / scale_mean))
+    print(f"{label}: " + ", ".join(f"{n} max/|max| {a:.2e} mean/|mean| {b:.2e}"
+                                   for n, (a, b) in summary.items()), flush=True)
+    for name, (a, b) in summary.items():
+        assert a <= BWD_MAX_REL, f"{label} {name}: max rel {a:.3e}"
+        assert b <= BWD_MEAN_REL, f"{label} {name}: mean rel {b:.3e}"
+
+
+def run_bwd(B, Hq, Hkv, Sq, Skv, D, mask, score, seed=0, window=100, prefix_len=70,
+            doc_lengths=(50, 130, 7, 113), softcap=1.5, scale=None):
+    label = f"bwd B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Skv{Skv} D{D} {mask} {score}"
+    q, k, v = workloads.randn_qkv(B, Hq, Hkv, Sq, Skv, D, "bf16", seed)
+    do = workloads.randn_qkv(B, Hq, Hkv, Sq, Skv, D, "bf16", seed + 1000)[0]
+    doc_ids = None
+    if has_document(mask):
+        lens = list(doc_lengths)
+        lens[-1] += Sq - sum(lens)
+        doc_ids = torch.from_numpy(workloads.doc_ids_from_lengths(lens, B))
+    dev = torch.device("cuda")
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    dd = doc_ids.to(dev) if doc_ids is not None else None
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    kw = dict(scale=scale, mask=mask, window=window, prefix_len=prefix_len, doc_ids=dd, score=score,
+              rel_scale=-0.05, softcap=softcap)
+    announce(label)
+    out, lse = af.attn_fwd(qd, kd, vd, **kw)
+    dq, dk, dv = af.attn_bwd(qd, kd, vd, out, lse, dod, **kw)
+    torch.cuda.synchronize()
+    ms = mask_spec(mask, window, prefix_len, doc_ids)
+    ss = oracle.ScoreSpec(workloads.SCORE_NAMES[score], rel_scale=-0.05, softcap=softcap)
+    ref = oracle.attention_backward_ref(f64(q), f64(k), f64(v), f64(do), scale, ms, ss)
+    compare_grads((dq, dk, dv), ref, label)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", MASKS)
+@pytest.mark.parametrize("score", SCORES)
+def test_bwd_small(D, mask, score):
+    run_bwd(2, 4, 2, 300, 300, D, mask, score, seed=D + len(mask) + len(score), window=37)
+
+
+@pytest.mark.parametrize("Sq,Skv", [(200, 333), (333, 200), (64, 1000), (1, 77), (77, 1)])
+@pytest.mark.parametrize("mask", ["none", "causal", "sliding", "prefix_lm"])
+def test_bwd_rectangular(Sq, Skv, mask):
+    run_bwd(1, 2, 1, Sq, Skv, 128, mask, "alibi", seed=Sq + Skv)
+
+
+@pytest.mark.parametrize("G", [1, 3, 8])
+def test_bwd_gqa_groups(G):
+    run_bwd(1, 2 * G, 2, 260, 260, 64, "causal", "none", seed=G)
+
+
+def test_bwd_deterministic():
+    dev = torch.device("cuda")
+    q, k, v = (t.to(dev) for t in workloads.randn_qkv(1, 8, 2, 700, 700, 128, "bf16", 3))
+    do = workloads.randn_qkv(1, 8, 2, 700, 700, 128, "bf16", 4)[0].to(dev)
+    announce("bwd deterministic")
+    out, lse = af.attn_fwd(q, k, v, mask="sliding", window=300, score="alibi")
+    g1 = af.attn_bwd(q, k, v, out, lse, do, mask="sliding", window=300, score="alibi")
+    g2 = af.attn_bwd(q, k, v, out, lse, do, mask="sliding", window=300, score="alibi")
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_bwd_rows_without_keys():
+    # sliding window 50 with Sq = 300 > Skv = 100: rows 149.. see no key
+    # (O = 0, LSE = -inf) and must give dQ = 0 and add nothing to dK, dV
+    dq, _, _ = run_bwd(1, 2, 1, 300, 100, 64, "sliding", "alibi", seed=8, window=50)
+    assert torch.all(dq[:, :, 149:] == 0)
+    # no key at all: zero dQ, empty dK and dV
+    dev = torch.device("cuda")
+    q, k, v = (t.to(dev) for t in workloads.randn_qkv(1, 2, 1, 50, 0, 64, "bf16", 5))
+    do = workloads.randn_qkv(1, 2, 1, 50, 0, 64, "bf16", 6)[0].to(dev)
+    announce("bwd no keys")
+    out, lse = af.attn_fwd(q, k, v)
+    dq, dk, dv = af.attn_bwd(q, k, v, out, lse, do)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and dk.numel() == 0 and dv.numel() == 0
+
+
+def test_bwd_causal_headline_shape_whole_heads():
+    w = workloads.CAUSAL_BF16
+    dev = torch.device("cuda")
+    q, k, v = workloads.randn_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, "bf16", w.seed)
+    do = workloads.randn_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, "bf16", w.seed + 1000)[0]
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    announce("bwd causal headline shape")
+    out, lse = af.attn_fwd(qd, kd, vd, mask="causal")
+    dq, dk, dv = af.attn_bwd(qd, kd, vd, out, lse, dod, mask="causal")
+    torch.cuda.synchronize()
+    for b, hq in ((0, 0), (w.B - 1, w.Hq - 1), (1, 7)):
+        sl = (slice(b, b + 1), slice(hq, hq + 1))
+        ref = oracle.attention_backward_ref(f64(q[sl]), f64(k[sl]), f64(v[sl]), f64(do[sl]),
+                                            1.0 / math.sqrt(w.D), oracle.MaskSpec(oracle.MASK_CAUSAL))
+        compare_grads((dq[sl], dk[sl], dv[sl]), ref, f"bwd causal headline b{b} h{hq}")

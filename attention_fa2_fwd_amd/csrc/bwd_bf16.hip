@@ -293,6 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     const char *kbase = kt + rd_tr;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      asm volatile("" ::: "memory");   // keep this chunk's LDS reads in the chunk
       const int kb = c >> 1;
       const int r0 = 8 * (c & 1);
       const u32x4 pw = {pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]), pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]),
@@ -371,6 +372,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __align__(16) float qv_lse0[kQTile], qv_lse1[kQTile];
   __shared__ __align__(16) float qv_dot0[kQTile], qv_dot1[kQTile];
   __shared__ __align__(16) int32_t qv_doc0[kQTile], qv_doc1[kQTile];
+  // V rows of each wave's 32 keys (the B operand of dP = dO V^T), read from
+  // LDS rather than held in registers; rows padded by 16 bytes so the 16
+  // lanes of a read group hit distinct banks.
+  constexpr int VROW = D * 2 + 16;
+  __shared__ __align__(16) char v_rows[4][32 * VROW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -392,17 +398,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int jlast = min(j0 + kKRows, a.Skv) - 1;
 
   const size_t kv_base = ((size_t)(b * a.Hkv + hkv) * a.Skv) * D;
-  // K and V rows as B operands: lane holds X[kj][16c + 8h .. + 7].
-  bf16x8 kf[NDC], vf[NDC];
+  // K rows as B operands in registers: lane holds K[kj][16c + 8h .. + 7].
+  // V rows go to this wave's LDS rows (32 rows x D, 16-byte chunks, rows
+  // past Skv repeat the last one); they are first read after the barrier
+  // that follows the prologue's loads.
+  bf16x8 kf[NDC];
   {
     const bf16x8 *ks = (const bf16x8 *)(a.k + kv_base + (size_t)kr * D);
-    const bf16x8 *vs = (const bf16x8 *)(a.v + kv_base + (size_t)kr * D);
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) {
-      kf[c] = ks[2 * c + h];
-      vf[c] = vs[2 * c + h];
+    for (int c = 0; c < NDC; ++c) kf[c] = ks[2 * c + h];
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int t = 0; t < 32 * CPR / 64; ++t) {
+      const int idx = 64 * t + lane;
+      const int r = idx / CPR, ch = idx % CPR;
+      const int key = min(jw0 + r, a.Skv - 1);
+      const bf16x8 x = *(const bf16x8 *)(a.v + kv_base + (size_t)key * D + 8 * ch);
+      *(bf16x8 *)(v_rows[wave] + r * VROW + 16 * ch) = x;
     }
   }
+  const char *vrow = v_rows[wave] + l32 * VROW + 16 * h;
   const float c_log2 = a.scale_log2;
   const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
   const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
@@ -496,9 +511,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     for (int c = 0; c < NDC; ++c) {
       const int o = rd_row + 32 * c;
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(qt_ + o), kf[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(ot + o), vf[c], dp, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(ot + o),
+                                                   *(const bf16x8 *)(vrow + 32 * c), dp, 0, 0, 0);
     }
-    float p[16];
+    // P and dS go to bf16 as soon as they are formed (two 16-query chunks of
+    // 8 values per lane each), which keeps the live set small.
+    uint32_t pw[8], sw[8];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qo = 8 * g + 4 * h;   // query offset of elements 4g .. 4g + 3
@@ -506,32 +524,33 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       const f32x4 d4 = *(const f32x4 *)(dt + qo);
       int4 c4 = int4{0, 0, 0, 0};
       if (DOC && !full) c4 = *(const int4 *)(dc + qo);
+      float pr[4], dr[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
         const int i = i0 + qo + e;
         const float x = mod_score<MOD>(s[r], c_log2, bias2, cap_k, cap2, i, kj);
-        float pr = fast_exp2(x - l4[e]);
+        float pe = fast_exp2(x - l4[e]);
         if (!full) {
           const int doc_i = (e == 0) ? c4.x : (e == 1) ? c4.y : (e == 2) ? c4.z : c4.w;
-          pr = pair_visible<MASK>(a.mask, i, kj, doc_i, doc_j) ? pr : 0.0f;
+          pe = pair_visible<MASK>(a.mask, i, kj, doc_i, doc_j) ? pe : 0.0f;
         }
-        p[r] = pr;
-        s[r] = pr * (dp[r] - d4[e]) * mod_grad<MOD>(x, inv_cap2);
+        pr[e] = pe;
+        dr[e] = pe * (dp[r] - d4[e]) * mod_grad<MOD>(x, inv_cap2);
       }
+      pw[2 * g] = pack_bf16x2(pr[0], pr[1]);
+      pw[2 * g + 1] = pack_bf16x2(pr[2], pr[3]);
+      sw[2 * g] = pack_bf16x2(dr[0], dr[1]);
+      sw[2 * g + 1] = pack_bf16x2(dr[2], dr[3]);
     }
     // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time.
     const char *obase = ot + rd_tr;
     const char *qbase = qt_ + rd_tr;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int r0 = 8 * c;
-      const u32x4 pw = {pack_bf16x2(p[r0 + 0], p[r0 + 1]), pack_bf16x2(p[r0 + 2], p[r0 + 3]),
-                        pack_bf16x2(p[r0 + 4], p[r0 + 5]), pack_bf16x2(p[r0 + 6], p[r0 + 7])};
-      const u32x4 sw = {pack_bf16x2(s[r0 + 0], s[r0 + 1]), pack_bf16x2(s[r0 + 2], s[r0 + 3]),
-                        pack_bf16x2(s[r0 + 4], s[r0 + 5]), pack_bf16x2(s[r0 + 6], s[r0 + 7])};
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-      const bf16x8 sb = __builtin_bit_cast(bf16x8, sw);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]});
+      const bf16x8 sb = __builtin_bit_cast(bf16x8, u32x4{sw[4 * c], sw[4 * c + 1], sw[4 * c + 2], sw[4 * c + 3]});
+      asm volatile("" ::: "memory");   // keep this chunk's LDS reads in the chunk
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const s16x4 olo = lds_read_tr(obase + T::off(16 * c) + 64 * db);

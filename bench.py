@@ -125,6 +125,39 @@ def bench_prefill(af, torch, workloads, w, steps, warmup, out_dtype=None, with_b
     return res
 
 
+def bench_backward(af, torch, workloads, w, steps, warmup):
+    """attn_bwd on a prefill workload (its forward run once for O and LSE).
+    Algorithmic FLOPs: 10 D per visible pair (the products S, dP, dV, dK,
+    dQ: 2.5 times the forward's), whatever the kernels recompute."""
+    dev = torch.device("cuda")
+    inp = workloads.prefill_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    do = workloads.randn_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.dtype, w.seed + 1000)[0].to(dev)
+    doc = inp["doc_ids"].to(dev) if inp["doc_ids"] is not None else None
+    kw = dict(scale=1.0 / math.sqrt(w.D), mask=w.mask, window=w.window, prefix_len=w.prefix_len,
+              doc_ids=doc, score=w.score, softcap=w.softcap)
+    out, lse = af.attn_fwd(q, k, v, **kw)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(int(af.load_library().attn_bwd_workspace_size(w.B, w.Hq, w.Sq)), 1),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        af.attn_bwd(q, k, v, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    e0 = t.event()
+    for _ in range(steps):
+        af.attn_bwd(q, k, v, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+    e1 = t.event()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = visible_pairs(w.mask, w.Sq, w.window, inp["doc_lengths"])
+    flops = 10.0 * w.D * w.B * w.Hq * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": ms, "tflops": tf, "gflop": flops / 1e9, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS}
+
+
 def bench_decode(af, torch, workloads, steps, warmup, window=0, score="none"):
     """Paged decode of the 64-sequence workload; with window > 0 each query
     sees its last `window` keys (and only those are counted as read)."""
@@ -201,7 +234,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     help="run one workload (dense, causal, gqa, document, causal_softcap, "
-                         "document_window, decode, decode_window) and exit")
+                         "document_window, decode, decode_window, bwd_causal, bwd_dense, "
+                         "bwd_gqa) and exit")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy, to calibrate byte counters")
     args = ap.parse_args()
@@ -236,6 +270,12 @@ def main():
                "gqa": workloads.GQA_WINDOW_ALIBI, "document": workloads.DOCUMENT_BLOCKMASK,
                "causal_softcap": workloads.CAUSAL_SOFTCAP,
                "document_window": workloads.DOC_WINDOW_BLOCKMASK}
+        if args.only in ("bwd_causal", "bwd_gqa", "bwd_dense"):
+            wl = {"bwd_causal": workloads.CAUSAL_BF16, "bwd_gqa": workloads.GQA_WINDOW_ALIBI,
+                  "bwd_dense": workloads.DENSE_BF16}[args.only]
+            r = bench_backward(af, torch, workloads, wl, args.steps, args.warmup)
+            print(json.dumps({"workload": args.only, **r}), flush=True)
+            return
         if args.only == "decode":
             r = bench_decode(af, torch, workloads, args.steps, args.warmup)
         elif args.only == "decode_window":
@@ -331,6 +371,10 @@ def main():
                         ("document_window1024_blockmask", workloads.DOC_WINDOW_BLOCKMASK)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             extra[name] = bench_prefill(af, torch, workloads, w, 20, 3)
+        for name, w in (("backward_causal_b4h16s2048d64", workloads.CAUSAL_BF16),
+                        ("backward_gqa_window1024_alibi", workloads.GQA_WINDOW_ALIBI)):
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            extra[name] = bench_backward(af, torch, workloads, w, 10, 2)
         print("[bench] paged decode", file=sys.stderr, flush=True)
         extra["paged_decode"] = bench_decode(af, torch, workloads, 20, 3)
         print("[bench] paged decode, window 1024 + alibi", file=sys.stderr, flush=True)

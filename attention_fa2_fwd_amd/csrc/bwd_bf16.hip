@@ -10,10 +10,10 @@
 // forward's LSE wherever it is needed.  With x = s Q K^T, S = score_mod(x)
 // masked, P = softmax(S) = exp(S - LSE):
 //
-//   D_i = sum_d dO_id O_id                       (bwd_row_dot_kernel)
+//   D_i = sum_d dO_id O_id                       (bwd_dq_kernel, stored)
 //   dP  = dO V^T,  dS = P (dP - D),  dX = dS score_mod'(x)
 //   dQ  = s dX K                                 (bwd_dq_kernel)
-//   dV  = P^T dO,  dK = s dX^T Q                 (bwd_dkdv_kernel)
+//   dV  = P^T dO,  dK = s dX^T Q                 (bwd_dkdv_kernel, after it)
 //
 // The two main kernels reuse the forward kernel's MFMA conventions
 // (v_mfma_f32_32x32x16_bf16, 4 waves x 32 rows, LDS tiles of 1 KiB row
@@ -25,6 +25,7 @@
 //    lane then holds one query and 16 keys, so LSE and D are one register
 //    each, and dS^T leaves the accumulator already in the B-operand layout of
 //    dQ^T += K^T dS^T, whose A operand is the transposed read of the K tile.
+//    It also forms each row's D from its O and dO rows and stores it.
 //  * bwd_dkdv_kernel, one workgroup per (b, hkv, 128 keys), streams 32-row
 //    tiles of Q and dO for every query head of the GQA group, so dK and dV
 //    sum the group in registers.  S = Q K^T and dP = dO V^T take Q and dO
@@ -68,8 +69,9 @@ struct Tile {
 };
 
 struct BwdArgs {
-  const __bf16 *q, *k, *v, *dout;
-  const float *lse, *row_dot;
+  const __bf16 *q, *k, *v, *out, *dout;
+  const float *lse;
+  float *row_dot;   // D per query row: written by the dQ kernel, read by the dK/dV kernel
   float *dq, *dk, *dv;
   int B, Hq, Hkv, Sq, Skv;
   float scale, scale_log2;
@@ -131,27 +133,6 @@ __device__ __forceinline__ float mod_grad(float x, float inv_cap2) {
 }
 
 // ---------------------------------------------------------------------------
-// D_i = sum_d dO_id O_id, one row per CPR lanes (CPR = D / 8 divides 64).
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_row_dot_kernel(const __bf16 *o, const __bf16 *dout,
-                                                                float *row_dot, long rows) {
-  constexpr int CPR = D / 8;
-  const long t = (long)blockIdx.x * kThreads + threadIdx.x;
-  const long row = t / CPR;
-  const int c = (int)(t % CPR);
-  float acc = 0.0f;
-  if (row < rows) {
-    const bf16x8 x = *(const bf16x8 *)(o + row * D + 8 * c);
-    const bf16x8 g = *(const bf16x8 *)(dout + row * D + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)g[e], acc);
-  }
-#pragma unroll
-  for (int w = CPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
-  if (row < rows && c == 0) row_dot[row] = acc;
-}
-
-// ---------------------------------------------------------------------------
 // dQ: one workgroup per (b, hq, 128 query rows); wave w owns rows
 // q0 + 32w .. + 31, lane (h, l32) the query q0 + 32w + l32.
 template <int D, int MASK, int MOD>
@@ -202,7 +183,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   const size_t row = (size_t)(b * a.Hq + hq) * a.Sq + qr;
   const float lse2 = a.lse[row] * kLog2e;
-  const float dsum = a.row_dot[row];
+  // D = sum_d dO O over the row: each lane half holds every other 8-wide
+  // chunk of it.  Stored for the dK/dV kernel.
+  float dsum;
+  {
+    const bf16x8 *os = (const bf16x8 *)(a.out + q_base + (size_t)qr * D);
+    float part = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+      const bf16x8 o8 = os[2 * c + h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)o8[e], (float)df[c][e], part);
+    }
+    dsum = part + __shfl_xor(part, 32);
+  }
+  if (h == 0 && qi < a.Sq) a.row_dot[row] = dsum;
   const float c_log2 = a.scale_log2;
   const float bias2 = (MOD == kModAdd) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
   const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
@@ -646,6 +641,7 @@ hipError_t launch_d(const BwdParams &p, hipStream_t stream) {
   a.q = (const __bf16 *)p.q;
   a.k = (const __bf16 *)p.k;
   a.v = (const __bf16 *)p.v;
+  a.out = (const __bf16 *)p.out;
   a.dout = (const __bf16 *)p.dout;
   a.lse = p.lse;
   a.row_dot = p.row_dot;
@@ -661,14 +657,6 @@ hipError_t launch_d(const BwdParams &p, hipStream_t stream) {
   a.scale_log2 = p.scale * kLog2e;
   a.mask = p.mask;
   a.score = p.score;
-  const long rows = (long)p.B * p.Hq * p.Sq;
-  if (rows > 0) {
-    const long threads = rows * (D / 8);
-    hipLaunchKernelGGL(bwd_row_dot_kernel<D>, dim3((unsigned)((threads + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, (const __bf16 *)p.out, a.dout, p.row_dot, rows);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   if (p.score.kind == ATTN_SCORE_SOFTCAP) return launch_mask<D, kModCap>(a, stream);
   return launch_mask<D, kModAdd>(a, stream);
 }

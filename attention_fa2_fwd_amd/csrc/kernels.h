@@ -29,7 +29,7 @@ struct BwdParams {
   const void *q, *k, *v, *out, *dout;   // bf16
   const float *lse;
   float *dq, *dk, *dv;
-  float *row_dot;   // workspace [B, Hq, Sq]: sum_d dO * O
+  float *row_dot;   // workspace [B, Hq, Sq]: sum_d dO * O, formed by the dQ kernel
   int B, Hq, Hkv, Sq, Skv, D;
   float scale;
   MaskArgs mask;

@@ -48,7 +48,7 @@ from .attention import (  # noqa: F401
     softmax_naive, softmax_safe3, softmax_online2,
     attention_rows, attention_ref, attention_bruteforce, attention_one_pass,
 )
-from .block_mask import block_mask_ref, block_mask_bruteforce  # noqa: F401
+from .block_mask import block_mask_ref, block_mask_cols_ref, block_mask_bruteforce  # noqa: F401
 from .backward import attention_backward_ref, attention_backward_rows, softmax_row_dot_ref  # noqa: F401
 from .paged_decode import (  # noqa: F401
     gather_paged_kv, paged_decode_ref, split_partials_ref, lse_combine_ref,

@@ -14,7 +14,10 @@ taken here:
 * kv_full[b, 0, qb, n] = 1 when every (i, j) of the listed block is visible
   (the kernel may then skip the per-element predicate);
 * unused tail entries are kv_indices = -1 and kv_full = 0;
-* the head axis has size 1: no mask kind here depends on the head.
+* the head axis has size 1: no mask kind here depends on the head;
+* the backward also needs the lists the other way round, per key block the
+  ascending query blocks (block_mask_cols_ref): the same (block, block)
+  incidence, transposed.
 
 Only the mask decides sparsity (no score modifier produces -inf).
 """
@@ -49,6 +52,33 @@ def block_mask_ref(mask: MaskSpec, batch: int, sq: int, skv: int,
                     full[b, 0, qb, n] = 1 if blk.all() else 0
                     n += 1
             num[b, 0, qb] = n
+    return num, idx, full
+
+
+def block_mask_cols_ref(mask: MaskSpec, batch: int, sq: int, skv: int,
+                        q_block: int = 128, kv_block: int = 128):
+    """The same blocks listed by key block, for the backward's key-stationary
+    pass: (q_num_blocks int32 [B,1,nKVB], q_indices int32 [B,1,nKVB,nQB]
+    ascending with -1 tails, q_full uint8 [B,1,nKVB,nQB] with 0 tails), from
+    the element-wise visibility grid."""
+    nqb = -(-sq // q_block)
+    nkb = -(-skv // kv_block)
+    num = np.zeros((batch, 1, nkb), dtype=np.int32)
+    idx = np.full((batch, 1, nkb, nqb), -1, dtype=np.int32)
+    full = np.zeros((batch, 1, nkb, nqb), dtype=np.uint8)
+    rows = np.arange(sq)
+    for b in range(batch):
+        for kb in range(nkb):
+            cols = np.arange(kb * kv_block, min(skv, (kb + 1) * kv_block))
+            vis = visible(mask, b, rows, cols)
+            n = 0
+            for qb in range(nqb):
+                blk = vis[qb * q_block:min(sq, (qb + 1) * q_block), :]
+                if blk.any():
+                    idx[b, 0, kb, n] = qb
+                    full[b, 0, kb, n] = 1 if blk.all() else 0
+                    n += 1
+            num[b, 0, kb] = n
     return num, idx, full
 
 

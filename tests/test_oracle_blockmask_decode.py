@@ -51,6 +51,38 @@ def test_block_mask_matches_scalar_scan(ci):
         assert np.array_equal(g, w)
 
 
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_block_mask_cols_are_the_transposed_incidence(ci):
+    # per key block, the query blocks whose row list holds it, same full flag;
+    # checked against the scalar scan's row lists
+    mask, b, sq, skv, qb, kb = CASES[ci]
+    rnum, ridx, rfull = oracle.block_mask_bruteforce(mask.kind, b, sq, skv, qb, kb, mask.window,
+                                                     mask.prefix_len, mask.doc_ids, mask.and_kinds)
+    cnum, cidx, cfull = oracle.block_mask_cols_ref(mask, b, sq, skv, qb, kb)
+    nqb, nkb = rnum.shape[2], cnum.shape[2]
+    for bb in range(b):
+        inc = {}
+        for q in range(nqb):
+            for n in range(rnum[bb, 0, q]):
+                inc[(q, int(ridx[bb, 0, q, n]))] = int(rfull[bb, 0, q, n])
+        for k in range(nkb):
+            want = sorted(q for (q, kk) in inc if kk == k)
+            got = [int(x) for x in cidx[bb, 0, k, :cnum[bb, 0, k]]]
+            assert got == want
+            assert [int(x) for x in cfull[bb, 0, k, :len(want)]] == [inc[(q, k)] for q in want]
+            assert np.all(cidx[bb, 0, k, len(want):] == -1) and np.all(cfull[bb, 0, k, len(want):] == 0)
+
+
+def test_block_mask_cols_causal_closed_form():
+    # causal, 16 x 16 blocks: key block kb is seen by query blocks kb..15,
+    # fully by kb+1..15
+    num, idx, full = oracle.block_mask_cols_ref(MaskSpec(MASK_CAUSAL), 1, 2048, 2048, 128, 128)
+    for kb in range(16):
+        assert num[0, 0, kb] == 16 - kb
+        assert list(idx[0, 0, kb, :16 - kb]) == list(range(kb, 16))
+        assert list(full[0, 0, kb, :16 - kb]) == [0] + [1] * (15 - kb)
+
+
 def test_block_mask_causal_counts_closed_form():
     num, idx, full = oracle.block_mask_ref(MaskSpec(MASK_CAUSAL), 1, 2048, 2048, 128, 128)
     n = 2048 // 128

@@ -30,8 +30,9 @@ F32, BF16 = 0, 1
 MASK_KINDS = {"none": 0, "causal": 1, "sliding": 2, "prefix_lm": 3, "document": 4}
 MASK_AND = 5   # masks joined with "&", e.g. "sliding&document&causal"
 SCORE_KINDS = {"none": 0, "alibi": 1, "rel_pos": 2, "softcap": 3}
-EXPORTED = ("attn_fwd", "attn_build_block_mask", "attn_paged_decode_workspace_size",
-            "attn_paged_decode", "attn_bwd_workspace_size", "attn_bwd", "attn_last_error")
+EXPORTED = ("attn_fwd", "attn_build_block_mask", "attn_block_mask_transpose",
+            "attn_paged_decode_workspace_size", "attn_paged_decode", "attn_bwd_workspace_size",
+            "attn_bwd", "attn_last_error")
 
 
 class AttnError(RuntimeError):
@@ -54,7 +55,9 @@ class BlockMaskC(ctypes.Structure):
     _fields_ = [("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
                 ("kv_full", ctypes.c_void_p), ("q_block", ctypes.c_int32),
                 ("kv_block", ctypes.c_int32), ("n_q_blocks", ctypes.c_int32),
-                ("n_kv_blocks", ctypes.c_int32), ("batch", ctypes.c_int32)]
+                ("n_kv_blocks", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("q_num_blocks", ctypes.c_void_p), ("q_indices", ctypes.c_void_p),
+                ("q_full", ctypes.c_void_p)]
 
 
 @dataclass
@@ -64,12 +67,17 @@ class BlockMask:
     kv_full: Optional[torch.Tensor]  # uint8 [B, 1, nQB, nKVB]
     q_block: int
     kv_block: int
+    # the same blocks listed by key block (attn_block_mask_transpose), for attn_bwd
+    q_num_blocks: Optional[torch.Tensor] = None   # int32 [B, 1, nKVB]
+    q_indices: Optional[torch.Tensor] = None      # int32 [B, 1, nKVB, nQB]
+    q_full: Optional[torch.Tensor] = None         # uint8 [B, 1, nKVB, nQB]
 
     def to_c(self) -> BlockMaskC:
         b, _, nqb, nkb = self.kv_indices.shape
         return BlockMaskC(self.kv_num_blocks.data_ptr(), self.kv_indices.data_ptr(),
                           self.kv_full.data_ptr() if self.kv_full is not None else None,
-                          self.q_block, self.kv_block, nqb, nkb, b)
+                          self.q_block, self.kv_block, nqb, nkb, b, _ptr(self.q_num_blocks),
+                          _ptr(self.q_indices), _ptr(self.q_full))
 
 
 _lib = None
@@ -97,11 +105,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       i32, i32, f32, i32, ctypes.POINTER(MaskParams), i32,
                                       ctypes.POINTER(ScoreParams), vp, ctypes.c_size_t, vp]
     lib.attn_paged_decode.restype = i32
+    lib.attn_block_mask_transpose.argtypes = [ctypes.POINTER(BlockMaskC), vp, vp, vp, vp]
+    lib.attn_block_mask_transpose.restype = i32
     lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                              f32, i32, ctypes.POINTER(MaskParams), i32, ctypes.POINTER(ScoreParams),
-                             vp, ctypes.c_size_t, vp]
+                             ctypes.POINTER(BlockMaskC), vp, ctypes.c_size_t, vp]
     lib.attn_bwd.restype = i32
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
@@ -211,6 +221,23 @@ def attn_build_block_mask(mask: str, B: int, Sq: int, Skv: int, *, q_block: int 
     return BlockMask(num, idx, full, q_block, kv_block)
 
 
+def attn_block_mask_transpose(bm: BlockMask) -> BlockMask:
+    """The BlockMask with its lists by key block filled in (for attn_bwd)."""
+    lib = load_library()
+    b, _, nqb, nkb = bm.kv_indices.shape
+    dev = bm.kv_indices.device
+    qnum = torch.empty((b, 1, nkb), dtype=torch.int32, device=dev)
+    qidx = torch.empty((b, 1, nkb, nqb), dtype=torch.int32, device=dev)
+    qfull = torch.empty((b, 1, nkb, nqb), dtype=torch.uint8, device=dev)
+    _need_device(bm.kv_num_blocks, bm.kv_indices, bm.kv_full, qnum, qidx, qfull)
+    c = bm.to_c()
+    rc = lib.attn_block_mask_transpose(ctypes.byref(c), qnum.data_ptr(), qidx.data_ptr(),
+                                       qfull.data_ptr(), _stream(dev))
+    _check("attn_block_mask_transpose", rc)
+    return BlockMask(bm.kv_num_blocks, bm.kv_indices, bm.kv_full, bm.q_block, bm.kv_block,
+                     qnum, qidx, qfull)
+
+
 def attn_paged_decode_workspace_size(num_seqs: int, Hq: int, D: int, max_pages_per_seq: int,
                                      page_size: int = 16) -> int:
     return int(load_library().attn_paged_decode_workspace_size(num_seqs, Hq, D,
@@ -258,8 +285,8 @@ def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optio
 
 def attn_bwd(q, k, v, out, lse, dout, *, scale: Optional[float] = None, mask: str = "none",
              window: int = 0, prefix_len: int = 0, doc_ids=None, score: str = "none",
-             alibi_slopes=None, rel_scale: float = 1.0, softcap: float = 0.0, workspace=None,
-             dq=None, dk=None, dv=None):
+             alibi_slopes=None, rel_scale: float = 1.0, softcap: float = 0.0,
+             block_mask: Optional[BlockMask] = None, workspace=None, dq=None, dk=None, dv=None):
     """Gradients of attn_fwd from its output and LSE.  q, out, dout
     [B,Hq,Sq,D] and k, v [B,Hkv,Skv,D] bf16; lse [B,Hq,Sq] float32.  Returns
     (dq, dk, dv) float32.  The mask and score arguments are the forward's."""
@@ -282,9 +309,13 @@ def attn_bwd(q, k, v, out, lse, dout, *, scale: Optional[float] = None, mask: st
         scale = 1.0 / math.sqrt(d)
     mk, mp = _mask_params(mask, window, prefix_len, doc_ids)
     sk, sp = _score_params(score, alibi_slopes, rel_scale, softcap)
+    if block_mask is not None and block_mask.q_indices is None:
+        block_mask = attn_block_mask_transpose(block_mask)
+    bmc = block_mask.to_c() if block_mask is not None else None
     rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                       dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), BF16, b, hq, hkv,
                       sq, skv, d, float(scale), mk, ctypes.byref(mp), sk, ctypes.byref(sp),
+                      ctypes.byref(bmc) if bmc is not None else None,
                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                       _stream(q.device))
     _check("attn_bwd", rc)

@@ -267,6 +267,31 @@ int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
   return launch_result(attn::launch_paged_decode(p, (hipStream_t)stream), "attn_paged_decode");
 }
 
+int attn_block_mask_transpose(const attn_block_mask_t *bm, int32_t *q_num_blocks, int32_t *q_indices,
+                              uint8_t *q_full, void *stream) {
+  if (!bm) return fail(ATTN_ERR_INVALID, "null block mask");
+  if (bm->batch < 0 || bm->n_q_blocks < 0 || bm->n_kv_blocks < 0)
+    return fail(ATTN_ERR_INVALID, "negative block mask shape");
+  if (bm->batch == 0 || bm->n_kv_blocks == 0) {
+    g_err[0] = '\0';
+    return ATTN_OK;
+  }
+  if (!q_num_blocks || (bm->n_q_blocks > 0 && !q_indices)) return fail(ATTN_ERR_INVALID, "null output pointer");
+  if (bm->n_q_blocks > 0 && (!bm->kv_num_blocks || !bm->kv_indices))
+    return fail(ATTN_ERR_INVALID, "block mask needs kv_num_blocks and kv_indices");
+  attn::BlockMaskTransposeParams p{};
+  p.num = bm->kv_num_blocks;
+  p.idx = bm->kv_indices;
+  p.full = bm->kv_full;
+  p.q_num = q_num_blocks;
+  p.q_idx = q_indices;
+  p.q_full = q_full;
+  p.batch = bm->batch;
+  p.nqb = bm->n_q_blocks;
+  p.nkb = bm->n_kv_blocks;
+  return launch_result(attn::launch_block_mask_transpose(p, (hipStream_t)stream), "attn_block_mask_transpose");
+}
+
 size_t attn_bwd_workspace_size(int B, int Hq, int Sq) {
   if (B <= 0 || Hq <= 0 || Sq <= 0) return 0;
   return ((size_t)B * Hq * Sq * sizeof(float) + 255) / 256 * 256;
@@ -275,8 +300,8 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Sq) {
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
              const void *dout, float *dq, float *dk, float *dv, attn_dtype_t dt, int B, int Hq, int Hkv,
              int Sq, int Skv, int D, float scale, attn_mask_kind_t mk, const attn_mask_params_t *mp,
-             attn_score_kind_t sk, const attn_score_params_t *sp, void *workspace,
-             size_t workspace_bytes, void *stream) {
+             attn_score_kind_t sk, const attn_score_params_t *sp, const attn_block_mask_t *bm,
+             void *workspace, size_t workspace_bytes, void *stream) {
   if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || D <= 0)
     return fail(ATTN_ERR_INVALID, "negative size (B=%d Hq=%d Hkv=%d Sq=%d Skv=%d D=%d)", B, Hq,
                 Hkv, Sq, Skv, D);
@@ -293,6 +318,30 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
   rc = check_score(sk, sp, &p.score);
   if (rc) return rc;
   if (!(scale == scale)) return fail(ATTN_ERR_INVALID, "scale is NaN");
+  if (bm) {
+    if (!bm->kv_num_blocks || !bm->kv_indices || !bm->q_num_blocks || !bm->q_indices)
+      return fail(ATTN_ERR_INVALID, "the backward needs the block mask lists both ways "
+                                    "(attn_block_mask_transpose writes the ones by key block)");
+    if (bm->q_block != 128 || bm->kv_block != 128)
+      return fail(ATTN_ERR_UNSUPPORTED, "block mask must use 128 x 128 blocks (got %d x %d)",
+                  bm->q_block, bm->kv_block);
+    if (bm->n_q_blocks != (Sq + 127) / 128 || bm->n_kv_blocks != (Skv + 127) / 128)
+      return fail(ATTN_ERR_INVALID, "block mask shape %d x %d does not match Sq=%d Skv=%d",
+                  bm->n_q_blocks, bm->n_kv_blocks, Sq, Skv);
+    if (bm->n_kv_blocks > 1024 || bm->n_q_blocks > 1024)
+      return fail(ATTN_ERR_UNSUPPORTED, "block mask with more than 1024 blocks a side");
+    if (bm->batch != 1 && bm->batch != B)
+      return fail(ATTN_ERR_INVALID, "block mask batch %d must be 1 or B=%d", bm->batch, B);
+    p.bm_num = bm->kv_num_blocks;
+    p.bm_idx = bm->kv_indices;
+    p.bm_full = bm->kv_full;
+    p.bm_qnum = bm->q_num_blocks;
+    p.bm_qidx = bm->q_indices;
+    p.bm_qfull = bm->q_full;
+    p.bm_nqb = bm->n_q_blocks;
+    p.bm_nkb = bm->n_kv_blocks;
+    p.bm_batch = bm->batch;
+  }
   if (B == 0 || Hq == 0 || (Sq == 0 && Skv == 0)) {
     g_err[0] = '\0';
     return ATTN_OK;

@@ -202,7 +202,87 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(BMArgs a) {
   if (tid == 0) a.num[row] = count;
 }
 
+// The lists by key block: one workgroup per (batch, key block), one query
+// block per thread.  A query block lists key block kb if its ascending row
+// list holds kb (binary search); the column is compacted with the same wave
+// ballots, so it comes out ascending.
+struct BMTArgs {
+  const int32_t *num, *idx;
+  const uint8_t *full;
+  int32_t *q_num, *q_idx;
+  uint8_t *q_full;
+  int nqb, nkb;
+};
+
+__global__ __launch_bounds__(kThreads) void block_mask_transpose_kernel(BMTArgs a) {
+  __shared__ int32_t wave_cnt[kThreads / 64];
+  __shared__ int32_t running;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kb = blockIdx.x;
+  const int b = blockIdx.y;
+  const size_t col = (size_t)b * a.nkb + kb;
+  int32_t *idx_col = a.q_idx + col * a.nqb;
+  uint8_t *full_col = a.q_full ? a.q_full + col * a.nqb : nullptr;
+  if (tid == 0) running = 0;
+  __syncthreads();
+  for (int base = 0; base < a.nqb; base += kThreads) {
+    const int qb = base + tid;
+    bool listed = false, full = false;
+    if (qb < a.nqb) {
+      const size_t row = (size_t)b * a.nqb + qb;
+      const int n = min(max(a.num[row], 0), a.nkb);
+      const int32_t *list = a.idx + row * a.nkb;
+      int lo = 0, hi = n - 1;
+      while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        const int v = list[mid];
+        if (v == kb) {
+          listed = true;
+          full = a.full && a.full[row * a.nkb + mid] != 0;
+          break;
+        }
+        if (v < kb) lo = mid + 1; else hi = mid - 1;
+      }
+    }
+    const unsigned long long ball = __ballot(listed);
+    const int rank_in_wave = __popcll(ball & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_cnt[wave] = __popcll(ball);
+    __syncthreads();
+    int off = running;
+    for (int w = 0; w < wave; ++w) off += wave_cnt[w];
+    if (listed) {
+      idx_col[off + rank_in_wave] = qb;
+      if (full_col) full_col[off + rank_in_wave] = full ? 1 : 0;
+    }
+    __syncthreads();
+    if (tid == 0) running += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+    __syncthreads();
+  }
+  const int count = running;
+  for (int n = count + tid; n < a.nqb; n += kThreads) {
+    idx_col[n] = -1;
+    if (full_col) full_col[n] = 0;
+  }
+  if (tid == 0) a.q_num[col] = count;
+}
+
 }  // namespace
+
+hipError_t launch_block_mask_transpose(const BlockMaskTransposeParams &p, hipStream_t stream) {
+  BMTArgs a;
+  a.num = p.num;
+  a.idx = p.idx;
+  a.full = p.full;
+  a.q_num = p.q_num;
+  a.q_idx = p.q_idx;
+  a.q_full = p.q_full;
+  a.nqb = p.nqb;
+  a.nkb = p.nkb;
+  hipLaunchKernelGGL(block_mask_transpose_kernel, dim3(p.nkb, p.batch), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_block_mask(const BlockMaskParams &p, hipStream_t stream) {
   BMArgs a;

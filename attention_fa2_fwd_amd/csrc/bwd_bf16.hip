@@ -35,7 +35,9 @@
 //    from the same LDS tiles.  Per-query LSE and D are staged in LDS with the
 //    tile.
 // Tiles without a visible pair are skipped and the predicate is dropped on
-// tiles where every pair is visible, from the mask's closed-form bounds.
+// tiles where every pair is visible, from the mask's closed-form bounds or,
+// given a BlockMask, from its lists: by query block for the dQ pass, by key
+// block for the dK/dV pass, staged in LDS.
 #include "kernels.h"
 
 namespace attn {
@@ -49,6 +51,7 @@ constexpr int kQRows = 128;        // query rows per dQ workgroup
 constexpr int kKTile = 64;         // key rows per tile in the dQ kernel
 constexpr int kKRows = 128;        // keys per dK/dV workgroup
 constexpr int kQTile = 32;         // query rows per tile in the dK/dV kernel
+constexpr int kListCap = 1024;     // BlockMask entries staged in LDS (host-checked)
 // Score forms: additive (raw scores or a bias) or the soft cap.
 constexpr int kModAdd = 0, kModCap = 1;
 
@@ -77,6 +80,10 @@ struct BwdArgs {
   float scale, scale_log2;
   MaskArgs mask;
   ScoreArgs score;
+  // BlockMask (bm_num == nullptr: closed-form tile ranges), 128 x 128 blocks
+  const int32_t *bm_num, *bm_idx, *bm_qnum, *bm_qidx;
+  const uint8_t *bm_full, *bm_qfull;
+  int bm_nqb, bm_nkb, bm_batch;
 };
 
 __device__ __forceinline__ s16x4 lds_read_tr(const char *p) {
@@ -147,6 +154,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __align__(16) char v_lds1[T::BYTES];
   __shared__ __align__(16) int32_t kdoc0[kKTile];
   __shared__ __align__(16) int32_t kdoc1[kKTile];
+  __shared__ int32_t s_blk[kListCap];
+  __shared__ uint8_t s_full[kListCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -210,19 +219,45 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
 
-  // Key tiles of the workgroup's rows.
-  const int qlast = min(q0 + kQRows, a.Sq) - 1;
-  int lo = 0, hi = a.Skv;
-  if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
-    hi = min(a.Skv, qlast + 1);
-  } else if (WIN) {
-    hi = min(a.Skv, qlast + 1);
-    lo = max(0, q0 - a.mask.window + 1);
-  } else if (MASK == ATTN_MASK_PREFIX_LM) {
-    hi = min(a.Skv, max(qlast + 1, a.mask.prefix_len));
+  // Key tiles of the workgroup's rows: the BlockMask row of this 128-row
+  // query block (two 64-key tiles per listed block), or a closed-form range.
+  const bool use_bm = a.bm_num != nullptr;
+  int n_tiles = 0, t_first = 0;
+  if (use_bm) {
+    const int bb = (a.bm_batch == 1) ? 0 : b;
+    const size_t brow = (size_t)bb * a.bm_nqb + qt;
+    // Counts and indices are device data: clamped, so a malformed list can
+    // only drop tiles, never address outside K / V.
+    const int n_blocks = min(max(a.bm_num[brow], 0), min(a.bm_nkb, kListCap));
+    n_tiles = 2 * n_blocks;
+    for (int t = tid; t < n_blocks; t += kThreads) {
+      s_blk[t] = a.bm_idx[brow * a.bm_nkb + t];
+      s_full[t] = a.bm_full ? a.bm_full[brow * a.bm_nkb + t] : 0;
+    }
+    __syncthreads();
+  } else {
+    const int qlast = min(q0 + kQRows, a.Sq) - 1;
+    int lo = 0, hi = a.Skv;
+    if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
+      hi = min(a.Skv, qlast + 1);
+    } else if (WIN) {
+      hi = min(a.Skv, qlast + 1);
+      lo = max(0, q0 - a.mask.window + 1);
+    } else if (MASK == ATTN_MASK_PREFIX_LM) {
+      hi = min(a.Skv, max(qlast + 1, a.mask.prefix_len));
+    }
+    t_first = lo / kKTile;
+    n_tiles = (hi > lo) ? (hi + kKTile - 1) / kKTile - t_first : 0;
   }
-  const int t_first = lo / kKTile;
-  const int n_tiles = (hi > lo) ? (hi + kKTile - 1) / kKTile - t_first : 0;
+  auto tile_key0 = [&](int n) __attribute__((always_inline)) -> int {
+    if (use_bm) {
+      const int blk = s_blk[n >> 1];
+      if (blk < 0 || blk >= a.bm_nkb) return a.Skv;   // an empty tile
+      return blk * 128 + (n & 1) * kKTile;
+    }
+    return (t_first + n) * kKTile;
+  };
+  auto tile_flag = [&](int n) __attribute__((always_inline)) -> bool { return use_bm && s_full[n >> 1] != 0; };
 
   const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.k + kv_base), (short)0, a.Skv * D * 2, kBufferFlags);
@@ -251,9 +286,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int tr_j = lane & 15;
   const int rd_tr = T::off(4 * h + (tr_j >> 2)) + (16 * ((lane >> 4) & 1) + 4 * (tr_j & 3)) * 2;
 
-  auto tile_step = [&](int k0, const char *kt, const char *vt, const int32_t *kdoc) __attribute__((always_inline)) {
-    if (block_empty<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1) || qw0 >= a.Sq) return;
-    const bool full = block_full<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1) && (k0 + kKTile <= a.Skv);
+  auto tile_step = [&](int k0, bool flag, const char *kt, const char *vt, const int32_t *kdoc)
+      __attribute__((always_inline)) {
+    if (block_empty<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1) || qw0 >= a.Sq || k0 >= a.Skv) return;
+    const bool full = (flag || block_full<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1)) && (k0 + kKTile <= a.Skv);
     // S^T and dP^T for the two 32-key blocks.
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -309,22 +345,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   // tile n - 1 used, computes tile n, then waits for its loads and meets
   // the other waves at the barrier.
   if (n_tiles > 0) {
-    load_tile(k_lds0, k_rsrc, t_first * kKTile);
-    load_tile(v_lds0, v_rsrc, t_first * kKTile);
-    if (DOC && wave == 0) kdoc0[lane] = load_doc(t_first * kKTile);
+    load_tile(k_lds0, k_rsrc, tile_key0(0));
+    load_tile(v_lds0, v_rsrc, tile_key0(0));
+    if (DOC && wave == 0) kdoc0[lane] = load_doc(tile_key0(0));
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
   auto iteration = [&](int n, char *k_cur, char *v_cur, int32_t *d_cur, char *k_nxt, char *v_nxt,
                        int32_t *d_nxt) __attribute__((always_inline)) {
-    const int k0 = (t_first + n) * kKTile;
+    const int k0 = tile_key0(n);
     int doc_fill = 0;
     if (n + 1 < n_tiles) {
-      load_tile(k_nxt, k_rsrc, k0 + kKTile);
-      load_tile(v_nxt, v_rsrc, k0 + kKTile);
-      if (DOC && wave == 0) doc_fill = load_doc(k0 + kKTile);
+      const int k1 = tile_key0(n + 1);
+      load_tile(k_nxt, k_rsrc, k1);
+      load_tile(v_nxt, v_rsrc, k1);
+      if (DOC && wave == 0) doc_fill = load_doc(k1);
     }
-    tile_step(k0, k_cur, v_cur, d_cur);
+    tile_step(k0, tile_flag(n), k_cur, v_cur, d_cur);
     if (DOC && wave == 0 && n + 1 < n_tiles) d_nxt[lane] = doc_fill;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -372,6 +409,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // lanes of a read group hit distinct banks.
   constexpr int VROW = D * 2 + 16;
   __shared__ __align__(16) char v_rows[4][32 * VROW];
+  __shared__ int32_t s_qblk[kListCap];
+  __shared__ uint8_t s_qfull[kListCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -427,25 +466,52 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
 
-  // Query tiles that may see the workgroup's keys [j0, jlast].
-  int lo = 0, hi = a.Sq - 1;
-  if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
-    lo = j0;
-  } else if (WIN) {
-    lo = j0;
-    hi = min(a.Sq - 1, jlast + a.mask.window - 1);
-  } else if (MASK == ATTN_MASK_PREFIX_LM) {
-    lo = (j0 < a.mask.prefix_len) ? 0 : j0;
+  // Query tiles that may see the workgroup's keys [j0, jlast]: the
+  // BlockMask column of this 128-key block (four 32-row tiles per listed
+  // query block), or a closed-form range.
+  const bool use_bm = a.bm_num != nullptr;
+  int n_qt = 0, t_first = 0;
+  if (use_bm) {
+    const int bb = (a.bm_batch == 1) ? 0 : b;
+    const size_t bcol = (size_t)bb * a.bm_nkb + kt;
+    const int n_blocks = min(max(a.bm_qnum[bcol], 0), min(a.bm_nqb, kListCap));
+    n_qt = 4 * n_blocks;
+    for (int t = tid; t < n_blocks; t += kThreads) {
+      s_qblk[t] = a.bm_qidx[bcol * a.bm_nqb + t];
+      s_qfull[t] = a.bm_qfull ? a.bm_qfull[bcol * a.bm_nqb + t] : 0;
+    }
+    __syncthreads();
+  } else {
+    int lo = 0, hi = a.Sq - 1;
+    if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
+      lo = j0;
+    } else if (WIN) {
+      lo = j0;
+      hi = min(a.Sq - 1, jlast + a.mask.window - 1);
+    } else if (MASK == ATTN_MASK_PREFIX_LM) {
+      lo = (j0 < a.mask.prefix_len) ? 0 : j0;
+    }
+    t_first = lo / kQTile;
+    n_qt = (hi >= lo) ? hi / kQTile + 1 - t_first : 0;
   }
-  const int t_first = lo / kQTile;
-  const int n_qt = (hi >= lo) ? hi / kQTile + 1 - t_first : 0;
   const int n_iter = n_qt * G;   // (query head, query tile) pairs
 
   // Loads of a (head, tile) pair: Q and dO rows into LDS by buffer_load ...
   // lds (rows past Sq read as zero), the per-query values by wave 0.
   const int ld_off = ((wave + T::NB * (lane / T::CPR)) * D + (lane % T::CPR) * 8) * 2;
   auto head_of = [&](int it) __attribute__((always_inline)) { return hkv * G + it / n_qt; };
-  auto tile_q0 = [&](int it) __attribute__((always_inline)) { return (t_first + it % n_qt) * kQTile; };
+  auto tile_q0 = [&](int it) __attribute__((always_inline)) -> int {
+    const int t = it % n_qt;
+    if (use_bm) {
+      const int blk = s_qblk[t >> 2];
+      if (blk < 0 || blk >= a.bm_nqb) return a.Sq;   // rows past Sq: no effect
+      return blk * 128 + (t & 3) * kQTile;
+    }
+    return (t_first + t) * kQTile;
+  };
+  auto tile_flag = [&](int it) __attribute__((always_inline)) -> bool {
+    return use_bm && s_qfull[(it % n_qt) >> 2] != 0;
+  };
   auto load_tiles = [&](int it, char *qd, char *od) __attribute__((always_inline)) {
     const int hq = head_of(it);
     const size_t base = ((size_t)(b * a.Hq + hq) * a.Sq) * D;
@@ -495,8 +561,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
                        const int32_t *dc) __attribute__((always_inline)) {
     const int i0 = tile_q0(it);
     const int i1 = i0 + kQTile - 1;
-    if (jw0 >= a.Skv || block_empty<MASK>(a.mask, i0, i1, jw0, jw1)) return;
-    const bool full = block_full<MASK>(a.mask, i0, i1, jw0, jw1);
+    if (jw0 >= a.Skv || i0 >= a.Sq || block_empty<MASK>(a.mask, i0, i1, jw0, jw1)) return;
+    const bool full = tile_flag(it) || block_full<MASK>(a.mask, i0, i1, jw0, jw1);
     const int hq = head_of(it);
     const float bias2 = (MOD == kModAdd) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
     // S = Q K^T and dP = dO V^T for the 32 queries: element r is query
@@ -657,6 +723,15 @@ hipError_t launch_d(const BwdParams &p, hipStream_t stream) {
   a.scale_log2 = p.scale * kLog2e;
   a.mask = p.mask;
   a.score = p.score;
+  a.bm_num = p.bm_num;
+  a.bm_idx = p.bm_idx;
+  a.bm_full = p.bm_full;
+  a.bm_qnum = p.bm_qnum;
+  a.bm_qidx = p.bm_qidx;
+  a.bm_qfull = p.bm_qfull;
+  a.bm_nqb = p.bm_nqb;
+  a.bm_nkb = p.bm_nkb;
+  a.bm_batch = p.bm_batch;
   if (p.score.kind == ATTN_SCORE_SOFTCAP) return launch_mask<D, kModCap>(a, stream);
   return launch_mask<D, kModAdd>(a, stream);
 }

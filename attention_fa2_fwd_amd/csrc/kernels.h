@@ -34,6 +34,11 @@ struct BwdParams {
   float scale;
   MaskArgs mask;
   ScoreArgs score;
+  // BlockMask, 128 x 128 blocks (bm_num == nullptr: closed-form tile ranges):
+  // lists by query block for the dQ pass, by key block for the dK/dV pass.
+  const int32_t *bm_num, *bm_idx, *bm_qnum, *bm_qidx;
+  const uint8_t *bm_full, *bm_qfull;
+  int bm_nqb, bm_nkb, bm_batch;
 };
 // Backward from the stored LSE, bf16 inputs, fp32 gradients, D in {64, 128}.
 hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t stream);
@@ -48,6 +53,15 @@ struct BlockMaskParams {
   uint8_t *full;
 };
 hipError_t launch_block_mask(const BlockMaskParams &p, hipStream_t stream);
+
+struct BlockMaskTransposeParams {
+  const int32_t *num, *idx;   // lists by query block [batch, nqb(, nkb)]
+  const uint8_t *full;        // may be null
+  int32_t *q_num, *q_idx;     // lists by key block [batch, nkb(, nqb)]
+  uint8_t *q_full;            // may be null
+  int batch, nqb, nkb;
+};
+hipError_t launch_block_mask_transpose(const BlockMaskTransposeParams &p, hipStream_t stream);
 
 struct DecodeParams {
   const void *q, *k_cache, *v_cache;

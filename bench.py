@@ -136,7 +136,14 @@ def bench_backward(af, torch, workloads, w, steps, warmup):
     doc = inp["doc_ids"].to(dev) if inp["doc_ids"] is not None else None
     kw = dict(scale=1.0 / math.sqrt(w.D), mask=w.mask, window=w.window, prefix_len=w.prefix_len,
               doc_ids=doc, score=w.score, softcap=w.softcap)
-    out, lse = af.attn_fwd(q, k, v, **kw)
+    bm = None
+    if w.block_mask:
+        # built once and reused, as for the forward; the lists by key block too
+        bm = af.attn_block_mask_transpose(
+            af.attn_build_block_mask(w.mask, w.B, w.Sq, w.Skv, window=w.window, prefix_len=w.prefix_len,
+                                     doc_ids=doc, device=dev))
+    out, lse = af.attn_fwd(q, k, v, block_mask=bm, **kw)
+    kw["block_mask"] = bm
     dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
     dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
     dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
@@ -235,7 +242,7 @@ def main():
     ap.add_argument("--only", default=None,
                     help="run one workload (dense, causal, gqa, document, causal_softcap, "
                          "document_window, decode, decode_window, bwd_causal, bwd_dense, "
-                         "bwd_gqa) and exit")
+                         "bwd_gqa, bwd_document) and exit")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy, to calibrate byte counters")
     args = ap.parse_args()
@@ -270,9 +277,10 @@ def main():
                "gqa": workloads.GQA_WINDOW_ALIBI, "document": workloads.DOCUMENT_BLOCKMASK,
                "causal_softcap": workloads.CAUSAL_SOFTCAP,
                "document_window": workloads.DOC_WINDOW_BLOCKMASK}
-        if args.only in ("bwd_causal", "bwd_gqa", "bwd_dense"):
+        if args.only in ("bwd_causal", "bwd_gqa", "bwd_dense", "bwd_document"):
             wl = {"bwd_causal": workloads.CAUSAL_BF16, "bwd_gqa": workloads.GQA_WINDOW_ALIBI,
-                  "bwd_dense": workloads.DENSE_BF16}[args.only]
+                  "bwd_dense": workloads.DENSE_BF16,
+                  "bwd_document": workloads.DOCUMENT_BLOCKMASK}[args.only]
             r = bench_backward(af, torch, workloads, wl, args.steps, args.warmup)
             print(json.dumps({"workload": args.only, **r}), flush=True)
             return
@@ -372,7 +380,8 @@ def main():
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             extra[name] = bench_prefill(af, torch, workloads, w, 20, 3)
         for name, w in (("backward_causal_b4h16s2048d64", workloads.CAUSAL_BF16),
-                        ("backward_gqa_window1024_alibi", workloads.GQA_WINDOW_ALIBI)):
+                        ("backward_gqa_window1024_alibi", workloads.GQA_WINDOW_ALIBI),
+                        ("backward_document_blockmask", workloads.DOCUMENT_BLOCKMASK)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             extra[name] = bench_backward(af, torch, workloads, w, 10, 2)
         print("[bench] paged decode", file=sys.stderr, flush=True)

@@ -117,6 +117,14 @@ typedef struct {
   const int32_t *kv_indices;
   const uint8_t *kv_full;
   int32_t q_block, kv_block, n_q_blocks, n_kv_blocks, batch;
+  /* The same incidence by key block, for attn_bwd's key-stationary pass
+   * (attn_block_mask_transpose writes them; attn_fwd ignores them):
+   *   q_num_blocks[b, 0, kb]   number of query blocks that list kb
+   *   q_indices[b, 0, kb, n]   those query blocks, ascending; -1 past the count
+   *   q_full[b, 0, kb, n]      their full flags; may be NULL                 */
+  const int32_t *q_num_blocks;
+  const int32_t *q_indices;
+  const uint8_t *q_full;
 } attn_block_mask_t;
 
 /* attn_fwd — fused attention forward, one pass with online softmax.
@@ -161,6 +169,19 @@ int attn_build_block_mask(attn_mask_kind_t mk, const attn_mask_params_t *mp, int
                           int Skv, int q_block, int kv_block, int32_t *kv_num_blocks,
                           int32_t *kv_indices, uint8_t *kv_full, void *stream);
 
+/* attn_block_mask_transpose — the lists of bm by key block (bm->q_*):
+ * per key block kb, the ascending query blocks whose kv_indices hold kb and
+ * their kv_full flags.  The backward's key-stationary pass walks these.
+ * Reads bm->kv_num_blocks / kv_indices (ascending, as attn_build_block_mask
+ * writes them) / kv_full (may be NULL: all flags 0); writes
+ *   q_num_blocks int32 [batch, 1, n_kv_blocks]
+ *   q_indices    int32 [batch, 1, n_kv_blocks, n_q_blocks], -1 tails
+ *   q_full       uint8 [batch, 1, n_kv_blocks, n_q_blocks], 0 tails; may be NULL
+ * device memory, caller-owned.  Errors: -1 for null pointers or a negative
+ * shape.                                                                    */
+int attn_block_mask_transpose(const attn_block_mask_t *bm, int32_t *q_num_blocks, int32_t *q_indices,
+                              uint8_t *q_full, void *stream);
+
 /* attn_bwd_workspace_size — bytes of device scratch attn_bwd needs: one
  * float per query row, B * Hq * Sq * 4, rounded up to 256.                  */
 size_t attn_bwd_workspace_size(int B, int Hq, int Sq);
@@ -182,14 +203,19 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Sq);
  *   workspace: device scratch of at least attn_bwd_workspace_size(B, Hq, Sq)
  *   bytes, 256-byte aligned; caller-owned, contents on entry do not matter.
  * A row with no visible key contributes nothing.  Supported: dt = BF16,
- * D in {64, 128} (others return -2).  No BlockMask argument: tiles are
- * skipped from each mask's closed-form bounds, document ids are compared
- * per element.  Errors as attn_fwd, plus -4 for a short workspace.         */
+ * D in {64, 128} (others return -2).
+ *   bm: NULL, or the forward's BlockMask (128 x 128 blocks) with its lists
+ *   by key block filled in (attn_block_mask_transpose): the dQ pass walks
+ *   kv_indices, the dK/dV pass q_indices, and full flags drop the
+ *   predicate.  It must describe the mask mk / mp (it only selects blocks).
+ *   Without it, tiles are chosen from each mask's closed-form bounds and
+ *   document ids are compared per element over the causal range.
+ * Errors as attn_fwd, plus -4 for a short workspace.                        */
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
              const void *dout, float *dq, float *dk, float *dv, attn_dtype_t dt, int B, int Hq, int Hkv,
              int Sq, int Skv, int D, float scale, attn_mask_kind_t mk, const attn_mask_params_t *mp,
-             attn_score_kind_t sk, const attn_score_params_t *sp, void *workspace,
-             size_t workspace_bytes, void *stream);
+             attn_score_kind_t sk, const attn_score_params_t *sp, const attn_block_mask_t *bm,
+             void *workspace, size_t workspace_bytes, void *stream);
 
 /* attn_paged_decode_workspace_size — bytes of device scratch attn_paged_decode
  * needs for this shape: fp32 partial outputs and log-sum-exps of every key

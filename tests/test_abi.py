@@ -144,3 +144,42 @@ def test_paged_decode_checks():
         rows = 2 * 8 * splits
         assert need == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
     assert lib.attn_paged_decode_workspace_size(0, 8, 128, 4, 16) == 0
+
+
+def _bwd(lib, dt=1, B=1, Hq=4, Hkv=2, Sq=16, Skv=16, D=64, mk=0, window=0, sk=0, bm=None,
+         ws=None, ws_bytes=0, null_tensors=True):
+    mp = af.MaskParams(window, 0, None, 0)
+    sp = af.ScoreParams(None, 1.0, 0.0)
+    return lib.attn_bwd(None, None, None, None, None, None, None, None, None, dt, B, Hq, Hkv, Sq, Skv,
+                        D, 0.125, mk, ctypes.byref(mp), sk, ctypes.byref(sp),
+                        ctypes.byref(bm) if bm is not None else None, ws, ws_bytes, None)
+
+
+def test_bwd_checks():
+    lib = af.load_library()
+    assert _bwd(lib, dt=0) == -2                      # bf16 only
+    assert _bwd(lib, D=96) == -2
+    assert _bwd(lib, Hq=3) == -1
+    assert _bwd(lib, mk=2) == -1                      # window 0
+    assert _bwd(lib, sk=9) == -1
+    assert _bwd(lib, B=0) == 0
+    assert _bwd(lib) == -4                            # no workspace
+    assert _bwd(lib, ws=256, ws_bytes=1 << 20) == -1  # workspace given, null tensors
+    assert lib.attn_bwd_workspace_size(2, 3, 100) == (2 * 3 * 100 * 4 + 255) // 256 * 256
+    assert lib.attn_bwd_workspace_size(0, 3, 100) == 0
+    # a BlockMask without the lists by key block, or with other block sizes
+    half = af.BlockMaskC(8, 8, None, 128, 128, 1, 1, 1, None, None, None)
+    assert _bwd(lib, bm=half) == -1
+    both = af.BlockMaskC(8, 8, None, 64, 64, 1, 1, 1, 8, 8, None)
+    assert _bwd(lib, bm=both) == -2
+    wrong = af.BlockMaskC(8, 8, None, 128, 128, 2, 1, 1, 8, 8, None)
+    assert _bwd(lib, bm=wrong) == -1                  # 2 query blocks for Sq = 16
+
+
+def test_block_mask_transpose_checks():
+    lib = af.load_library()
+    assert lib.attn_block_mask_transpose(None, None, None, None, None) == -1
+    bm = af.BlockMaskC(None, None, None, 128, 128, 2, 2, 1, None, None, None)
+    assert lib.attn_block_mask_transpose(ctypes.byref(bm), None, None, None, None) == -1
+    empty = af.BlockMaskC(None, None, None, 128, 128, 2, 0, 1, None, None, None)
+    assert lib.attn_block_mask_transpose(ctypes.byref(empty), None, None, None, None) == 0

@@ -80,6 +80,24 @@ def test_block_mask_bit_exact(case):
     assert np.array_equal(bm.kv_full.cpu().numpy(), full)
 
 
+@pytest.mark.parametrize("case", range(len(BM_CASES)))
+def test_block_mask_transpose_bit_exact(case):
+    mask, B, Sq, Skv, qb, kb, kw = BM_CASES[case]
+    dev = torch.device("cuda")
+    doc = torch.from_numpy(_case_doc_ids(B, Sq, kw)) if has_document(mask) else None
+    announce(f"block mask transpose {BM_CASES[case][:6]}")
+    bm = af.attn_build_block_mask(mask, B, Sq, Skv, q_block=qb, kv_block=kb,
+                                  window=kw.get("window", 0), prefix_len=kw.get("prefix_len", 0),
+                                  doc_ids=doc.to(dev) if doc is not None else None, device=dev)
+    bt = af.attn_block_mask_transpose(bm)
+    torch.cuda.synchronize()
+    ms = mask_spec(mask, kw.get("window", 0), kw.get("prefix_len", 0), doc)
+    num, idx, full = oracle.block_mask_cols_ref(ms, B, Sq, Skv, qb, kb)
+    assert np.array_equal(bt.q_num_blocks.cpu().numpy(), num)
+    assert np.array_equal(bt.q_indices.cpu().numpy(), idx)
+    assert np.array_equal(bt.q_full.cpu().numpy(), full)
+
+
 def test_block_mask_document_window_workload():
     w = workloads.DOC_WINDOW_BLOCKMASK
     dev = torch.device("cuda")

@@ -59,8 +59,8 @@ def compare_grads(got, ref, label):
 
 
 def run_bwd(B, Hq, Hkv, Sq, Skv, D, mask, score, seed=0, window=100, prefix_len=70,
-            doc_lengths=(50, 130, 7, 113), softcap=1.5, scale=None):
-    label = f"bwd B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Skv{Skv} D{D} {mask} {score}"
+            doc_lengths=(50, 130, 7, 113), softcap=1.5, scale=None, block_mask=False):
+    label = f"bwd B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Skv{Skv} D{D} {mask} {score} bm={block_mask}"
     q, k, v = workloads.randn_qkv(B, Hq, Hkv, Sq, Skv, D, "bf16", seed)
     do = workloads.randn_qkv(B, Hq, Hkv, Sq, Skv, D, "bf16", seed + 1000)[0]
     doc_ids = None
@@ -76,7 +76,12 @@ def run_bwd(B, Hq, Hkv, Sq, Skv, D, mask, score, seed=0, window=100, prefix_len=
               rel_scale=-0.05, softcap=softcap)
     announce(label)
     out, lse = af.attn_fwd(qd, kd, vd, **kw)
-    dq, dk, dv = af.attn_bwd(qd, kd, vd, out, lse, dod, **kw)
+    bm = None
+    if block_mask:
+        bm = af.attn_block_mask_transpose(
+            af.attn_build_block_mask(mask, B, Sq, Skv, window=window, prefix_len=prefix_len, doc_ids=dd,
+                                     device=dev))
+    dq, dk, dv = af.attn_bwd(qd, kd, vd, out, lse, dod, block_mask=bm, **kw)
     torch.cuda.synchronize()
     ms = mask_spec(mask, window, prefix_len, doc_ids)
     ss = oracle.ScoreSpec(workloads.SCORE_NAMES[score], rel_scale=-0.05, softcap=softcap)
@@ -90,6 +95,18 @@ def run_bwd(B, Hq, Hkv, Sq, Skv, D, mask, score, seed=0, window=100, prefix_len=
 @pytest.mark.parametrize("score", SCORES)
 def test_bwd_small(D, mask, score):
     run_bwd(2, 4, 2, 300, 300, D, mask, score, seed=D + len(mask) + len(score), window=37)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", MASKS)
+def test_bwd_block_mask_path(D, mask):
+    """With the BlockMask the backward matches the oracle and, bit for bit,
+    the closed-form path (the extra tiles that path visits add exact zeros)."""
+    kw = dict(seed=11 + D, window=150, prefix_len=200, doc_lengths=(300, 41, 129, 1, 229))
+    g_bm = run_bwd(1, 4, 2, 700, 700, D, mask, "alibi", block_mask=True, **kw)
+    g_cf = run_bwd(1, 4, 2, 700, 700, D, mask, "alibi", **kw)
+    for a, b in zip(g_bm, g_cf):
+        assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("Sq,Skv", [(200, 333), (333, 200), (64, 1000), (1, 77), (77, 1)])

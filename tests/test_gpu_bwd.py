@@ -109,6 +109,31 @@ def test_bwd_block_mask_path(D, mask):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("mask", ["document", "sliding&document"])
+@pytest.mark.parametrize("block_mask", [False, True])
+def test_bwd_unsorted_document_ids(mask, block_mask):
+    # ids drawn at random from 5 values: neither sorted nor contiguous
+    B, Hq, Hkv, S, D = 1, 4, 2, 400, 64
+    q, k, v = workloads.randn_qkv(B, Hq, Hkv, S, S, D, "bf16", 21)
+    do = workloads.randn_qkv(B, Hq, Hkv, S, S, D, "bf16", 22)[0]
+    ids = torch.from_numpy(np.random.default_rng(23).integers(0, 5, size=(B, S)).astype(np.int32))
+    dev = torch.device("cuda")
+    qd, kd, vd, dod, dd = q.to(dev), k.to(dev), v.to(dev), do.to(dev), ids.to(dev)
+    kw = dict(mask=mask, window=90, doc_ids=dd, score="rel_pos", rel_scale=-0.05)
+    label = f"bwd unsorted ids {mask} bm={block_mask}"
+    announce(label)
+    out, lse = af.attn_fwd(qd, kd, vd, **kw)
+    bm = None
+    if block_mask:
+        bm = af.attn_build_block_mask(mask, B, S, S, window=90, doc_ids=dd, device=dev)
+    grads = af.attn_bwd(qd, kd, vd, out, lse, dod, block_mask=bm, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward_ref(f64(q), f64(k), f64(v), f64(do), 1.0 / math.sqrt(D),
+                                        mask_spec(mask, 90, doc_ids=ids),
+                                        oracle.ScoreSpec(oracle.SCORE_REL_POS, rel_scale=-0.05))
+    compare_grads(grads, ref, label)
+
+
 @pytest.mark.parametrize("Sq,Skv", [(200, 333), (333, 200), (64, 1000), (1, 77), (77, 1)])
 @pytest.mark.parametrize("mask", ["none", "causal", "sliding", "prefix_lm"])
 def test_bwd_rectangular(Sq, Skv, mask):

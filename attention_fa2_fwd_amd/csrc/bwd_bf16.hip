@@ -166,7 +166,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int n_qtiles = (a.Sq + kQRows - 1) / kQRows;
   const int bh_count = a.B * a.Hq;
   const int qt = n_qtiles - 1 - (int)(blockIdx.x / bh_count);   // longest key ranges first
-  const int bh = (int)(blockIdx.x % bh_count);
+  // Workgroups go round-robin to the 8 XCDs; each XCD gets a contiguous run
+  // of heads, so the query heads of one kv head share an L2.
+  const int xh = (int)(blockIdx.x % bh_count);
+  const int bh = (bh_count % 8 == 0) ? (xh % 8) * (bh_count / 8) + xh / 8 : xh;
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
   const int hkv = (hq * a.Hkv) / a.Hq;

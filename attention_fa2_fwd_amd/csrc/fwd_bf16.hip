@@ -43,6 +43,9 @@
 //    only when a tile exceeds it by a margin; key tiles are visited last to
 //    first, so under causal-type masks and ALiBi the first tile already
 //    holds the row's largest scores; LSE in natural log on output.
+//  * The 8 XCDs (each with its own L2) take workgroups round-robin; the head
+//    index is permuted so that each XCD works on a contiguous run of heads,
+//    and the query heads of a GQA group read their K/V through one L2.
 //  * Causal-type masks: workgroups with the most key tiles are launched
 //    first; waves skip tiles that hold no visible key for their rows and
 //    skip the predicate on tiles where every key is visible.
@@ -137,7 +140,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // Heaviest query tiles first (causal-type masks give later tiles more keys).
   const int bh_count = a.B * a.Hq;
   const int qt = a.n_qtiles - 1 - (int)(blockIdx.x / bh_count);
-  const int bh = (int)(blockIdx.x % bh_count);
+  // Workgroups go round-robin to the 8 XCDs; each XCD gets a contiguous run
+  // of heads, so the query heads of one kv head share an L2.
+  const int xh = (int)(blockIdx.x % bh_count);
+  const int bh = (bh_count % 8 == 0) ? (xh % 8) * (bh_count / 8) + xh / 8 : xh;
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
   const int hkv = (hq * a.Hkv) / a.Hq;

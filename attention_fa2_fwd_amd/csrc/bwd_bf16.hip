@@ -52,8 +52,8 @@ constexpr int kKTile = 64;         // key rows per tile in the dQ kernel
 constexpr int kKRows = 128;        // keys per dK/dV workgroup
 constexpr int kQTile = 32;         // query rows per tile in the dK/dV kernel
 constexpr int kListCap = 1024;     // BlockMask entries staged in LDS (host-checked)
-// Score forms: additive (raw scores or a bias) or the soft cap.
-constexpr int kModAdd = 0, kModCap = 1;
+// Score forms: raw scores, a bias added, or the soft cap.
+constexpr int kModAdd = 0, kModCap = 1, kModRaw = 2;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -122,13 +122,16 @@ __device__ __forceinline__ bool block_full(const MaskArgs &m, int i0, int i1, in
   return false;
 }
 
-// Log2-domain modified score of raw dot product s for query i, key j, and
-// the factor score_mod'(x) of the chain rule.
+// Log2-domain modified score of raw dot product s, and the factor
+// score_mod'(x) of the chain rule.  With a bias, bias2 (j - i) is passed as
+// base + bias2 * off: base per tile and lane, off a compile-time offset of
+// the accumulator element, so the bias costs one FMA.
 template <int MOD>
 __device__ __forceinline__ float mod_score(float s, float c_log2, float bias2, float cap_k, float cap2,
-                                           int i, int j) {
+                                           float base, float off) {
   if (MOD == kModCap) return softcap_log2_fast(s, cap_k, cap2);
-  return __builtin_fmaf(s, c_log2, bias2 * (float)(j - i));
+  if (MOD == kModRaw) return s * c_log2;
+  return __builtin_fmaf(s, c_log2, __builtin_fmaf(bias2, off, base));
 }
 template <int MOD>
 __device__ __forceinline__ float mod_grad(float x, float inv_cap2) {
@@ -308,13 +311,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     }
     // dS^T element r of block kb: key j = k0 + 32 kb + 8 (r / 4) + 4h + r % 4.
     const int jb = k0 + 4 * h;
+    const float bias_base = bias2 * (float)(jb - qi);   // j - i = (jb - qi) + off
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
         const int j = jb + off;
-        const float x = mod_score<MOD>(s[kb][r], c_log2, bias2, cap_k, cap2, qi, j);
+        const float x = mod_score<MOD>(s[kb][r], c_log2, bias2, cap_k, cap2, bias_base, (float)off);
         float p = fast_exp2(x - lse2);
         if (!full) {
           const int doc_j = DOC ? kdoc[4 * h + off] : 0;
@@ -502,9 +506,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // Loads of a (head, tile) pair: Q and dO rows into LDS by buffer_load ...
   // lds (rows past Sq read as zero), the per-query values by wave 0.
   const int ld_off = ((wave + T::NB * (lane / T::CPR)) * D + (lane % T::CPR) * 8) * 2;
-  auto head_of = [&](int it) __attribute__((always_inline)) { return hkv * G + it / n_qt; };
-  auto tile_q0 = [&](int it) __attribute__((always_inline)) -> int {
-    const int t = it % n_qt;
+  // A step is one (query head, query tile) pair, heads outer; steps advance
+  // one at a time, so finding a step's head and tile needs no division.
+  struct Step {
+    int hq, t;
+  };
+  auto next_step = [&](Step st) __attribute__((always_inline)) -> Step {
+    return (st.t + 1 < n_qt) ? Step{st.hq, st.t + 1} : Step{st.hq + 1, 0};
+  };
+  auto tile_q0 = [&](int t) __attribute__((always_inline)) -> int {
     if (use_bm) {
       const int blk = s_qblk[t >> 2];
       if (blk < 0 || blk >= a.bm_nqb) return a.Sq;   // rows past Sq: no effect
@@ -512,17 +522,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
     return (t_first + t) * kQTile;
   };
-  auto tile_flag = [&](int it) __attribute__((always_inline)) -> bool {
-    return use_bm && s_qfull[(it % n_qt) >> 2] != 0;
+  auto tile_flag = [&](int t) __attribute__((always_inline)) -> bool {
+    return use_bm && s_qfull[t >> 2] != 0;
   };
-  auto load_tiles = [&](int it, char *qd, char *od) __attribute__((always_inline)) {
-    const int hq = head_of(it);
+  auto load_tiles = [&](Step st, char *qd, char *od) __attribute__((always_inline)) {
+    const int hq = st.hq;
     const size_t base = ((size_t)(b * a.Hq + hq) * a.Sq) * D;
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.q + base), (short)0, a.Sq * D * 2, kBufferFlags);
     const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.dout + base), (short)0, a.Sq * D * 2, kBufferFlags);
-    const int soff = __builtin_amdgcn_readfirstlane(tile_q0(it) * D * 2);
+    const int soff = __builtin_amdgcn_readfirstlane(tile_q0(st.t) * D * 2);
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)(qd + (4 * i + wave) * T::BLK), 16,
@@ -537,11 +547,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     float lse2, dot;
     int doc;
   };
-  auto fetch_qvals = [&](int it) __attribute__((always_inline)) -> QVals {
-    const int i = tile_q0(it) + lane;
+  auto fetch_qvals = [&](Step st) __attribute__((always_inline)) -> QVals {
+    const int i = tile_q0(st.t) + lane;
     QVals r{INFINITY, 0.0f, -1};
     if (lane < kQTile && i < a.Sq) {
-      const size_t row = (size_t)(b * a.Hq + head_of(it)) * a.Sq + i;
+      const size_t row = (size_t)(b * a.Hq + st.hq) * a.Sq + i;
       r.lse2 = a.lse[row] * kLog2e;
       r.dot = a.row_dot[row];
       if (DOC) r.doc = doc_row[i];
@@ -560,13 +570,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int tr_j = lane & 15;
   const int rd_tr = T::off(4 * h + (tr_j >> 2)) + (16 * ((lane >> 4) & 1) + 4 * (tr_j & 3)) * 2;
 
-  auto tile_step = [&](int it, const char *qt_, const char *ot, const float *ls, const float *dt,
+  auto tile_step = [&](Step st, const char *qt_, const char *ot, const float *ls, const float *dt,
                        const int32_t *dc) __attribute__((always_inline)) {
-    const int i0 = tile_q0(it);
+    const int i0 = tile_q0(st.t);
     const int i1 = i0 + kQTile - 1;
     if (jw0 >= a.Skv || i0 >= a.Sq || block_empty<MASK>(a.mask, i0, i1, jw0, jw1)) return;
-    const bool full = tile_flag(it) || block_full<MASK>(a.mask, i0, i1, jw0, jw1);
-    const int hq = head_of(it);
+    const bool full = tile_flag(st.t) || block_full<MASK>(a.mask, i0, i1, jw0, jw1);
+    const int hq = st.hq;
     const float bias2 = (MOD == kModAdd) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
     // S = Q K^T and dP = dO V^T for the 32 queries: element r is query
     // i0 + 8 (r / 4) + 4h + r % 4, key kj.
@@ -581,6 +591,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // P and dS go to bf16 as soon as they are formed (two 16-query chunks of
     // 8 values per lane each), which keeps the live set small.
     uint32_t pw[8], sw[8];
+    // j - i = (kj - i0 - 4h) - (8g + e) for element 4g + e
+    const float bias_base = bias2 * (float)(kj - i0 - 4 * h);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qo = 8 * g + 4 * h;   // query offset of elements 4g .. 4g + 3
@@ -593,7 +605,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
         const int i = i0 + qo + e;
-        const float x = mod_score<MOD>(s[r], c_log2, bias2, cap_k, cap2, i, kj);
+        const float x = mod_score<MOD>(s[r], c_log2, bias2, cap_k, cap2, bias_base, (float)(-(8 * g + e)));
         float pe = fast_exp2(x - l4[e]);
         if (!full) {
           const int doc_i = (e == 0) ? c4.x : (e == 1) ? c4.y : (e == 2) ? c4.z : c4.w;
@@ -631,32 +643,40 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
+  const Step first{hkv * G, 0};
   if (n_iter > 0) {
-    load_tiles(0, q_lds0, o_lds0);
-    if (wave == 0) store_qvals(fetch_qvals(0), qv_lse0, qv_dot0, qv_doc0);
+    load_tiles(first, q_lds0, o_lds0);
+    if (wave == 0) store_qvals(fetch_qvals(first), qv_lse0, qv_dot0, qv_doc0);
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
-  auto iteration = [&](int it, char *q_cur, char *o_cur, float *l_cur, float *d_cur, int32_t *c_cur,
-                       char *q_nxt, char *o_nxt, float *l_nxt, float *d_nxt, int32_t *c_nxt)
-      __attribute__((always_inline)) {
+  // Iteration it (step st): load step it + 1 into the buffers step it - 1
+  // used, compute step it, wait for this wave's loads, barrier.
+  auto iteration = [&](int it, Step st, char *q_cur, char *o_cur, float *l_cur, float *d_cur,
+                       int32_t *c_cur, char *q_nxt, char *o_nxt, float *l_nxt, float *d_nxt,
+                       int32_t *c_nxt) __attribute__((always_inline)) {
     QVals nv{INFINITY, 0.0f, -1};
     if (it + 1 < n_iter) {
-      load_tiles(it + 1, q_nxt, o_nxt);
-      if (wave == 0) nv = fetch_qvals(it + 1);
+      const Step nx = next_step(st);
+      load_tiles(nx, q_nxt, o_nxt);
+      if (wave == 0) nv = fetch_qvals(nx);
     }
-    tile_step(it, q_cur, o_cur, l_cur, d_cur, c_cur);
+    tile_step(st, q_cur, o_cur, l_cur, d_cur, c_cur);
     if (wave == 0 && it + 1 < n_iter) store_qvals(nv, l_nxt, d_nxt, c_nxt);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   int it = 0;
+  Step st = first;
   for (; it + 1 < n_iter; it += 2) {
-    iteration(it, q_lds0, o_lds0, qv_lse0, qv_dot0, qv_doc0, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1);
-    iteration(it + 1, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1, q_lds0, o_lds0, qv_lse0, qv_dot0, qv_doc0);
+    iteration(it, st, q_lds0, o_lds0, qv_lse0, qv_dot0, qv_doc0, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1);
+    st = next_step(st);
+    iteration(it + 1, st, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1, q_lds0, o_lds0, qv_lse0, qv_dot0,
+              qv_doc0);
+    st = next_step(st);
   }
   if (it < n_iter)
-    iteration(it, q_lds0, o_lds0, qv_lse0, qv_dot0, qv_doc0, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1);
+    iteration(it, st, q_lds0, o_lds0, qv_lse0, qv_dot0, qv_doc0, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1);
 
   // dK = s dX^T Q, dV = P^T dO: lane holds X^T[32 db + 8 g + 4h + e][kj].
   if (kj < a.Skv) {
@@ -736,6 +756,7 @@ hipError_t launch_d(const BwdParams &p, hipStream_t stream) {
   a.bm_nkb = p.bm_nkb;
   a.bm_batch = p.bm_batch;
   if (p.score.kind == ATTN_SCORE_SOFTCAP) return launch_mask<D, kModCap>(a, stream);
+  if (p.score.kind == ATTN_SCORE_NONE) return launch_mask<D, kModRaw>(a, stream);
   return launch_mask<D, kModAdd>(a, stream);
 }
 

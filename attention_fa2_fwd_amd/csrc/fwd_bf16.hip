@@ -58,6 +58,10 @@ namespace {
 
 constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // key rows per tile
+// Key tiles per BlockMask block: the host accepts only 128-wide key blocks on
+// this path, so a tile's block and part are a shift and a mask.
+constexpr int kTilesPerBlock = 128 / kBN;
+static_assert(kTilesPerBlock == 2, "block = tile index >> 1");
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kListCap = 1024; // BlockMask entries staged in LDS per query tile (host-checked)
 // Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
@@ -91,7 +95,7 @@ struct KernelArgs {
   ScoreArgs score;
   const int32_t *bm_num, *bm_idx;
   const uint8_t *bm_full;
-  int bm_nqb, bm_nkb, bm_batch, tiles_per_block;
+  int bm_nqb, bm_nkb, bm_batch;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     // Counts and indices are device data: clamp them so a malformed list
     // can only drop tiles, never address outside K/V.
     const int n_blocks = min(max(a.bm_num[row], 0), min(a.bm_nkb, kListCap));
-    n_tiles = n_blocks * a.tiles_per_block;
+    n_tiles = n_blocks * kTilesPerBlock;
     bm_list = a.bm_idx + row * a.bm_nkb;
     if (a.bm_full) bm_flags = a.bm_full + row * a.bm_nkb;
     for (int t = tid; t < n_blocks; t += kThreads) {
@@ -209,17 +213,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   auto tile_key0 = [&](int n) __attribute__((always_inline)) -> int {
     n = n_tiles - 1 - n;
     if (bm_list) {
-      const int bi = n / a.tiles_per_block;
+      const int bi = n >> 1;
       const int blk = s_blk[bi];   // bi < n_blocks <= kListCap
       if (blk < 0 || blk >= a.bm_nkb) return a.Skv;      // treated as an empty tile
-      return blk * (a.tiles_per_block * kBN) + (n % a.tiles_per_block) * kBN;
+      return blk * (kTilesPerBlock * kBN) + (n & 1) * kBN;
     }
     return (t_first + n) * kBN;
   };
   auto tile_block_full = [&](int n) __attribute__((always_inline)) -> bool {
     n = n_tiles - 1 - n;
     if (!bm_flags) return false;
-    const int bi = n / a.tiles_per_block;
+    const int bi = n >> 1;
     return s_full[bi] != 0;
   };
 
@@ -596,7 +600,6 @@ hipError_t launch_d(const FwdParams &p, hipStream_t stream) {
   a.bm_nqb = p.bm_nqb;
   a.bm_nkb = p.bm_nkb;
   a.bm_batch = p.bm_batch;
-  a.tiles_per_block = p.bm_num ? p.bm_kv_block / kBN : 1;
   const unsigned grid = (unsigned)(a.n_qtiles * p.B * p.Hq);
   if (p.score.kind == ATTN_SCORE_SOFTCAP) {
     return p.out_f32 ? launch_mask<D, kModCap, true>(a, p.mask.kind, grid, stream)

@@ -447,7 +447,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
           p0 = fast_exp2(__builtin_fmaf(s[kb][r0 + e], c_log2, -mu));
           p1 = fast_exp2(__builtin_fmaf(s[kb][r0 + e + 1], c_log2, -mu));
         }
-        ps[e >> 1] += p0 + p1;
+        // At D=64, where the VALU is the limit, the first chunk seeds the
+        // partial sums (0 + x is not folded away: it could change the sign
+        // of a zero), measured 1-4% faster; at D=128 the changed schedule
+        // measured 1-2% slower, so the sums start from zero there.
+        if (D == 64 && c == 0) ps[e >> 1] = p0 + p1; else ps[e >> 1] += p0 + p1;
         pw[e >> 1] = pack_bf16x2(p0, p1);
       }
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});

@@ -85,7 +85,9 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
 }
 
-__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
+// Three workgroups per CU (168 VGPRs, 48 KiB of LDS each) keep more pages
+// in flight than two: measured 0.6% faster unwindowed and 6% with a window.
+__global__ __launch_bounds__(kThreads, 3) void decode_split_kernel(DecArgs a) {
   // V pages staged per wave: three slots, three separate LDS objects.
   __shared__ __align__(16) char v_lds0[kWaves][kBlockBytes];
   __shared__ __align__(16) char v_lds1[kWaves][kBlockBytes];
@@ -337,32 +339,66 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecArgs a) {
 
 struct CombArgs {
   const int32_t *seq_lens;
+  int n_items;   // N * Hq
   int Hq, max_pages, max_splits, split_pages, window;
   const float *ws_o, *ws_lse;
   __bf16 *out;
   float *lse;
 };
 
-// One workgroup per (sequence, query head); thread d owns output column d.
-__global__ __launch_bounds__(kD) void decode_combine_kernel(CombArgs a) {
-  const int hq = blockIdx.x;
-  const int s = blockIdx.y;
-  const int d = threadIdx.x;
+// One wave per (sequence, query head).  The lanes take the splits' LSEs, 64
+// at a time, for the reference max M and the weight sum; lane l then owns
+// output columns 2l and 2l + 1 and accumulates the splits' partials with the
+// weights e^(lse_k - M), taken per split from the lane that holds them.
+constexpr int kCombWaves = 4;
+__global__ __launch_bounds__(64 * kCombWaves) void decode_combine_kernel(CombArgs a) {
+  static_assert(kD == 128, "two output columns per lane");
+  const int lane = threadIdx.x & 63;
+  const int item = (int)blockIdx.x * kCombWaves + (int)(threadIdx.x >> 6);   // s * Hq + hq
+  if (item >= a.n_items) return;                                            // uniform per wave
+  const int s = item / a.Hq;
   int t0, pf, pe;
   key_range(a.seq_lens[s], a.window, a.max_pages, t0, pf, pe);
-  const int ns = (pe - pf + a.split_pages - 1) / a.split_pages;
-  const size_t row0 = ((size_t)s * a.Hq + hq) * a.max_splits;
+  const int ns = __builtin_amdgcn_readfirstlane((pe - pf + a.split_pages - 1) / a.split_pages);
+  const size_t row0 = (size_t)item * a.max_splits;
   float M = -INFINITY;
-  for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ws_lse[row0 + k]);
-  float acc = 0.0f, tot = 0.0f;
-  for (int k = 0; k < ns; ++k) {
-    const float w = fast_exp2((a.ws_lse[row0 + k] - M) * kLog2e);
-    tot += w;
-    acc = fmaf(w, a.ws_o[(row0 + k) * kD + d], acc);
+  for (int k0 = 0; k0 < ns; k0 += 64)
+    if (k0 + lane < ns) M = fmaxf(M, a.ws_lse[row0 + k0 + lane]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float acc0 = 0.0f, acc1 = 0.0f, tot = 0.0f;
+  const f32x2 *po = (const f32x2 *)(a.ws_o + row0 * kD) + lane;
+  for (int k0 = 0; k0 < ns; k0 += 64) {
+    const float wl = (k0 + lane < ns) ? fast_exp2((a.ws_lse[row0 + k0 + lane] - M) * kLog2e) : 0.0f;
+    tot += wl;
+    const int kn = min(64, ns - k0);
+    auto take = [&](int j, f32x2 v) __attribute__((always_inline)) {
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), j));
+      acc0 = fmaf(w, v[0], acc0);
+      acc1 = fmaf(w, v[1], acc1);
+    };
+    int j = 0;
+    for (; j + 16 <= kn; j += 16) {   // sixteen independent row loads in flight
+      f32x2 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = po[(size_t)(k0 + j + u) * (kD / 2)];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) take(j + u, v[u]);
+    }
+    for (; j + 4 <= kn; j += 4) {
+      f32x2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = po[(size_t)(k0 + j + u) * (kD / 2)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) take(j + u, v[u]);
+    }
+    for (; j < kn; ++j) take(j, po[(size_t)(k0 + j) * (kD / 2)]);
   }
-  const size_t orow = (size_t)s * a.Hq + hq;
-  a.out[orow * kD + d] = (__bf16)((tot > 0.0f) ? acc / tot : 0.0f);
-  if (d == 0) a.lse[orow] = (tot > 0.0f) ? M + logf(tot) : -INFINITY;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+  const float inv = (tot > 0.0f) ? 1.0f / tot : 0.0f;
+  *(uint32_t *)(a.out + (size_t)item * kD + 2 * lane) = pack_bf16x2(acc0 * inv, acc1 * inv);
+  if (lane == 0) a.lse[item] = (tot > 0.0f) ? M + logf(tot) : -INFINITY;
 }
 
 }  // namespace
@@ -417,6 +453,7 @@ hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   CombArgs c;
   c.seq_lens = p.seq_lens;
+  c.n_items = p.N * p.Hq;
   c.Hq = p.Hq;
   c.max_pages = p.max_pages;
   c.max_splits = p.max_splits;
@@ -426,7 +463,8 @@ hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
   c.ws_lse = p.ws_lse;
   c.out = (__bf16 *)p.out;
   c.lse = p.lse;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.Hq, p.N), dim3(kD), 0, stream, c);
+  const unsigned comb_grid = (unsigned)((c.n_items + kCombWaves - 1) / kCombWaves);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(comb_grid), dim3(64 * kCombWaves), 0, stream, c);
   return hipGetLastError();
 }
 

@@ -52,6 +52,7 @@ constexpr int kKTile = 64;         // key rows per tile in the dQ kernel
 constexpr int kKRows = 128;        // keys per dK/dV workgroup
 constexpr int kQTile = 32;         // query rows per tile in the dK/dV kernel
 constexpr int kListCap = 1024;     // BlockMask entries staged in LDS (host-checked)
+static_assert(2 * kOrderCap <= kListCap, "work-ordering scratch fits the list buffer");
 // Score forms: raw scores, a bias added, or the soft cap.
 constexpr int kModAdd = 0, kModCap = 1, kModRaw = 2;
 
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __align__(16) char v_lds1[T::BYTES];
   __shared__ __align__(16) int32_t kdoc0[kKTile];
   __shared__ __align__(16) int32_t kdoc1[kKTile];
-  __shared__ int32_t s_blk[kListCap];
+  __shared__ __align__(16) int32_t s_blk[kListCap];
   __shared__ uint8_t s_full[kListCap];
 
   const int tid = threadIdx.x;
@@ -168,13 +169,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int n_qtiles = (a.Sq + kQRows - 1) / kQRows;
   const int bh_count = a.B * a.Hq;
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / bh_count);   // longest key ranges first
   // Workgroups go round-robin to the 8 XCDs; each XCD gets a contiguous run
   // of heads, so the query heads of one kv head share an L2.
   const int xh = (int)(blockIdx.x % bh_count);
   const int bh = (bh_count % 8 == 0) ? (xh % 8) * (bh_count / 8) + xh / 8 : xh;
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
+  // Longest key ranges first: the later query tiles, or with a BlockMask the
+  // tiles with the most listed blocks (ranked in the list buffer before the
+  // list is staged).
+  const int pos = (int)(blockIdx.x / bh_count);
+  int qt = n_qtiles - 1 - pos;
+  if (a.bm_num && n_qtiles <= kOrderCap) {
+    const int bb = (a.bm_batch == 1) ? 0 : b;
+    qt = work_ordered_tile(a.bm_num + (size_t)bb * a.bm_nqb, n_qtiles, min(a.bm_nkb, kListCap), pos, true,
+                           s_blk, tid, kThreads);
+  }
   const int hkv = (hq * a.Hkv) / a.Hq;
   const int q0 = qt * kQRows;
   const int qw0 = q0 + wave * 32;
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // lanes of a read group hit distinct banks.
   constexpr int VROW = D * 2 + 16;
   __shared__ __align__(16) char v_rows[4][32 * VROW];
-  __shared__ int32_t s_qblk[kListCap];
+  __shared__ __align__(16) int32_t s_qblk[kListCap];
   __shared__ uint8_t s_qfull[kListCap];
 
   const int tid = threadIdx.x;
@@ -430,10 +440,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int l32 = lane & 31;
 
   const int bh_count = a.B * a.Hkv;
-  const int kt = (int)(blockIdx.x / bh_count);   // first key tiles (most query tiles) first
   const int bh = (int)(blockIdx.x % bh_count);
   const int b = bh / a.Hkv;
   const int hkv = bh - b * a.Hkv;
+  // Most query tiles first: the first key tiles, or with a BlockMask the key
+  // blocks with the most listed query blocks (ties, the earlier block first;
+  // ranked in the list buffer before the list is staged).
+  const int pos = (int)(blockIdx.x / bh_count);
+  int kt = pos;
+  if (a.bm_num && a.bm_qnum) {
+    const int n_ktiles = (a.Skv + kKRows - 1) / kKRows;
+    if (n_ktiles <= kOrderCap) {
+      const int bb = (a.bm_batch == 1) ? 0 : b;
+      kt = work_ordered_tile(a.bm_qnum + (size_t)bb * a.bm_nkb, n_ktiles, min(a.bm_nqb, kListCap), pos,
+                             false, s_qblk, tid, kThreads);
+    }
+  }
   const int G = a.Hq / a.Hkv;
   const int j0 = kt * kKRows;
   const int jw0 = j0 + wave * 32;

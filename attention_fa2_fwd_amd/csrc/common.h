@@ -114,6 +114,42 @@ __device__ __forceinline__ float half_swap_sum(float v) {
   return a + b;
 }
 
+// Work-ordered dispatch for launches whose tiles come from BlockMask lists:
+// a tile's work is its listed block count, which need not follow the tile
+// index (documents).  Every workgroup of the launch ranks the same counts and
+// takes the tile at its dispatch position pos, in the order: descending count
+// (clamped to [0, cap], cap < 2^15), ties by tile index, the later tile first
+// when later_first.  The sort keys (count << 16 | tie) are distinct, so the
+// ranks form one permutation, identical in every workgroup.  Needs
+// n <= kOrderCap and 2 * kOrderCap ints of 16-byte aligned LDS scratch; every
+// thread of the workgroup calls it (it holds barriers).
+constexpr int kOrderCap = 256;
+__device__ inline int work_ordered_tile(const int32_t *cnt, int n, int cap, int pos, bool later_first,
+                                        int32_t *scratch, int tid, int nthreads) {
+  int32_t *s_key = scratch;
+  int32_t *s_order = scratch + kOrderCap;
+  const int n4 = (n + 3) & ~3;   // keys padded with INT_MIN to whole int4s
+  for (int t = tid; t < n4; t += nthreads) {
+    const int tie = later_first ? t : kOrderCap - 1 - t;
+    s_key[t] = (t < n) ? (min(max(cnt[t], 0), cap) << 16) | tie : INT_MIN;
+  }
+  __syncthreads();
+  for (int t = tid; t < n; t += nthreads) {
+    const int key = s_key[t];
+    int r = 0;
+#pragma unroll 4
+    for (int u = 0; u < n4; u += 4) {
+      const int4 v = *(const int4 *)&s_key[u];
+      r += (int)(v.x > key) + (int)(v.y > key) + (int)(v.z > key) + (int)(v.w > key);
+    }
+    s_order[r] = t;
+  }
+  __syncthreads();
+  const int tile = s_order[pos];
+  __syncthreads();   // scratch is free again for the caller
+  return tile;
+}
+
 // Round-to-nearest-even fp32 -> bf16 of two values, packed (lo = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 r = {(__bf16)a, (__bf16)b};

@@ -68,10 +68,7 @@ constexpr int kTilesPerBlock = 128 / kBN;
 static_assert(kTilesPerBlock == 2, "block = tile index >> 1");
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kListCap = 1024; // BlockMask entries staged in LDS per query tile (host-checked)
-// BlockMask launches with at most this many query tiles are dispatched in
-// order of work (the ranking's scratch lives in the list buffer).
-constexpr int kOrderCap = 256;
-static_assert(2 * kOrderCap <= kListCap, "ranking scratch fits the list buffer");
+static_assert(2 * kOrderCap <= kListCap, "work-ordering scratch fits the list buffer");
 // Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kKPad = 16;      // bytes between K row blocks
@@ -161,33 +158,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // work is its listed block count, which need not grow with the tile index
   // (documents): every workgroup ranks the tiles of its batch row by count
   // (descending; ties, the later tile first) and takes the tile at its
-  // dispatch position.  The sort keys (count << 16 | tile) are distinct, so
-  // the ranks form one permutation, identical in every workgroup.
+  // dispatch position (the ranking's scratch is the list buffer, free until
+  // the list is staged).
   const int pos = (int)(blockIdx.x / bh_count);
   int qt = a.n_qtiles - 1 - pos;
   if (a.bm_num && a.n_qtiles <= kOrderCap) {
     const int bb = (a.bm_batch == 1) ? 0 : b;
-    const int32_t *cnt = a.bm_num + (size_t)bb * a.bm_nqb;
-    int32_t *s_key = s_blk;               // the list buffer is free until the list is staged
-    int32_t *s_order = s_blk + kOrderCap;
-    const int cap = min(a.bm_nkb, kListCap);   // < 2^15
-    const int n4 = (a.n_qtiles + 3) & ~3;      // keys padded with INT_MIN to whole int4s
-    for (int t = tid; t < n4; t += kThreads)
-      s_key[t] = (t < a.n_qtiles) ? (min(max(cnt[t], 0), cap) << 16) | t : INT_MIN;
-    __syncthreads();
-    for (int t = tid; t < a.n_qtiles; t += kThreads) {
-      const int key = s_key[t];
-      int r = 0;
-#pragma unroll 4
-      for (int u = 0; u < n4; u += 4) {
-        const int4 v = *(const int4 *)&s_key[u];
-        r += (int)(v.x > key) + (int)(v.y > key) + (int)(v.z > key) + (int)(v.w > key);
-      }
-      s_order[r] = t;
-    }
-    __syncthreads();
-    qt = s_order[pos];
-    __syncthreads();   // every wave has its tile before the list overwrites s_blk
+    qt = work_ordered_tile(a.bm_num + (size_t)bb * a.bm_nqb, a.n_qtiles, min(a.bm_nkb, kListCap), pos,
+                           true, s_blk, tid, kThreads);
   }
   const int hkv = (hq * a.Hkv) / a.Hq;
   const int q0 = qt * kBM;

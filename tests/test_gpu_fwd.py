@@ -260,3 +260,63 @@ def test_full_size_sampled(w):
                                             rows=first)
             compare(f64(out)[:, :, first], f64(lse)[:, :, first], o_r, l_r, q.dtype,
                     w.name + " bf16-out first rows")
+
+
+def _two_batch_doc_ids(S):
+    """[2, S] document ids with a different layout in each batch row, so the
+    per-batch BlockMask rows (and their work order) differ."""
+    rows = []
+    for lens in ((100, 700, 37, S - 837), (600, 50, S - 650)):
+        rows.append(np.repeat(np.arange(len(lens), dtype=np.int32), lens))
+    return np.stack(rows).astype(np.int32)
+
+
+@pytest.mark.parametrize("mask", ["document", "sliding&document"])
+def test_block_mask_work_order_per_batch_rows(mask):
+    """BlockMask launches take query tiles in order of listed work, ranked per
+    batch row: with two different document layouts the result equals the
+    oracle and, bit for bit, the closed-form path."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 1000, 128
+    q, k, v = workloads.randn_qkv(B, Hq, Hkv, S, S, D, "bf16", 31)
+    ids = _two_batch_doc_ids(S)
+    dev = torch.device("cuda")
+    qd, kd, vd, dd = q.to(dev), k.to(dev), v.to(dev), torch.from_numpy(ids).to(dev)
+    label = f"work order per batch row {mask}"
+    announce(label)
+    bm = af.attn_build_block_mask(mask, B, S, S, window=300, doc_ids=dd, device=dev)
+    kw = dict(mask=mask, window=300, doc_ids=dd, score="alibi")
+    out_bm, lse_bm = af.attn_fwd(qd, kd, vd, block_mask=bm, **kw)
+    out_cf, lse_cf = af.attn_fwd(qd, kd, vd, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out_bm, out_cf) and torch.equal(lse_bm, lse_cf)
+    o_ref, l_ref = oracle.attention_ref(f64(q), f64(k), f64(v), 1.0 / math.sqrt(D),
+                                        mask_spec(mask, 300, doc_ids=ids),
+                                        oracle.ScoreSpec(oracle.SCORE_ALIBI))
+    compare(out_bm, lse_bm, o_ref, l_ref, q.dtype, label, out_rounding=True)
+
+
+@pytest.mark.parametrize("S", [32768, 33024])
+def test_block_mask_work_order_limit(S):
+    """Up to 256 query tiles the BlockMask launch ranks them by work; past
+    that it keeps the dispatch order.  Both equal the closed-form path bit
+    for bit (one head, causal, D=64)."""
+    q, k, v = workloads.randn_qkv(1, 1, 1, S, S, 64, "bf16", 41)
+    dev = torch.device("cuda")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    announce(f"work order limit S={S}")
+    bm = af.attn_build_block_mask("causal", 1, S, S, device=dev)
+    out_bm, lse_bm = af.attn_fwd(qd, kd, vd, mask="causal", block_mask=bm)
+    out_cf, lse_cf = af.attn_fwd(qd, kd, vd, mask="causal")
+    torch.cuda.synchronize()
+    assert torch.equal(out_bm, out_cf) and torch.equal(lse_bm, lse_cf)
+    # a few rows against the oracle (row i sees keys 0..i)
+    rows = [0, 1, 127, 128, S // 2, S - 1]
+    qs = f64(q)[0, 0, rows]
+    kk, vv = f64(k)[0, 0], f64(v)[0, 0]
+    for n, i in enumerate(rows):
+        s = (kk[: i + 1] @ qs[n]) / math.sqrt(64)
+        m = s.max()
+        p = np.exp(s - m)
+        o = (p @ vv[: i + 1]) / p.sum()
+        assert np.max(np.abs(out_bm[0, 0, i].float().cpu().numpy() - o)) <= 1e-2
+        assert abs(float(lse_bm[0, 0, i]) - (m + math.log(p.sum()))) <= 1e-3

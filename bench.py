@@ -242,7 +242,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="run one workload (dense, causal, gqa, document, causal_softcap, "
                          "document_window, decode, decode_window, bwd_causal, bwd_dense, "
-                         "bwd_gqa, bwd_document) and exit")
+                         "bwd_gqa, bwd_document; for scale: long_dense_d128, "
+                         "long_causal_d128, long_dense_d64) and exit")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy, to calibrate byte counters")
     args = ap.parse_args()
@@ -276,7 +277,10 @@ def main():
         sel = {"dense": workloads.DENSE_BF16, "causal": workloads.CAUSAL_BF16,
                "gqa": workloads.GQA_WINDOW_ALIBI, "document": workloads.DOCUMENT_BLOCKMASK,
                "causal_softcap": workloads.CAUSAL_SOFTCAP,
-               "document_window": workloads.DOC_WINDOW_BLOCKMASK}
+               "document_window": workloads.DOC_WINDOW_BLOCKMASK,
+               "long_dense_d128": workloads.LONG_DENSE_D128,
+               "long_causal_d128": workloads.LONG_CAUSAL_D128,
+               "long_dense_d64": workloads.LONG_DENSE_D64}
         if args.only in ("bwd_causal", "bwd_gqa", "bwd_dense", "bwd_document"):
             wl = {"bwd_causal": workloads.CAUSAL_BF16, "bwd_gqa": workloads.GQA_WINDOW_ALIBI,
                   "bwd_dense": workloads.DENSE_BF16,

@@ -89,6 +89,13 @@ DOC_WINDOW_BLOCKMASK = PrefillWorkload("document_window1024_blockmask_bf16_b1h16
 CAUSAL_SOFTCAP = PrefillWorkload("causal_softcap5_bf16_b4h16s2048d64", "bf16", 4, 16, 16, 2048, 2048,
                                  64, mask="causal", score="softcap", softcap=5.0)
 PAGED_DECODE = DecodeWorkload("paged_decode_bf16_n64hq32hkv8d128p16", 64, 32, 8, 128)
+# Longer launches of the same kernel, for scale only (timed, not parity
+# workloads): the GQA shape without window or bias, dense and causal, and the
+# dense D=64 shape at S=8192.
+LONG_DENSE_D128 = PrefillWorkload("long_dense_bf16_b2hq32hkv8s8192d128", "bf16", 2, 32, 8, 8192, 8192, 128)
+LONG_CAUSAL_D128 = PrefillWorkload("long_causal_bf16_b2hq32hkv8s8192d128", "bf16", 2, 32, 8, 8192, 8192,
+                                   128, mask="causal")
+LONG_DENSE_D64 = PrefillWorkload("long_dense_bf16_b2h32s8192d64", "bf16", 2, 32, 32, 8192, 8192, 64)
 
 PREFILL_WORKLOADS = [TINY_CAUSAL_F32, DENSE_BF16, CAUSAL_BF16, GQA_WINDOW_ALIBI, DOCUMENT_BLOCKMASK,
                      CAUSAL_SOFTCAP, DOC_WINDOW_BLOCKMASK]

@@ -39,7 +39,6 @@ int reduce_and(uint32_t bits) {
 }
 bool valid_score_kind(int sk) { return sk >= ATTN_SCORE_NONE && sk <= ATTN_SCORE_SOFTCAP; }
 
-// Shared checks of mask parameters; fills the kernel-side copy.
 // Shared checks of mask parameters; fills the kernel-side copy, with an AND
 // set reduced to the kind the kernels run.  The parameters of every kind in
 // the set are checked, also those the reduction drops.

@@ -204,15 +204,23 @@ def attn_fwd(q, k, v, *, scale: Optional[float] = None, mask: str = "none", wind
 
 def attn_build_block_mask(mask: str, B: int, Sq: int, Skv: int, *, q_block: int = 128,
                           kv_block: int = 128, window: int = 0, prefix_len: int = 0,
-                          doc_ids=None, device="cuda", with_full: bool = True) -> BlockMask:
-    """Build the BlockMask of a mask kind on the GPU."""
+                          doc_ids=None, device="cuda", with_full: bool = True,
+                          out: BlockMask = None) -> BlockMask:
+    """Build the BlockMask of a mask kind on the GPU (into `out`'s buffers
+    when given: a BlockMask of the same B, block sizes and block counts)."""
     lib = load_library()
     device = torch.device(device)
     nqb = -(-Sq // q_block)
     nkb = -(-Skv // kv_block)
-    num = torch.empty((B, 1, nqb), dtype=torch.int32, device=device)
-    idx = torch.empty((B, 1, nqb, nkb), dtype=torch.int32, device=device)
-    full = torch.empty((B, 1, nqb, nkb), dtype=torch.uint8, device=device) if with_full else None
+    if out is not None:
+        if (tuple(out.kv_indices.shape) != (B, 1, nqb, nkb) or out.q_block != q_block
+                or out.kv_block != kv_block or (out.kv_full is None) == with_full):
+            raise ValueError("out does not match the BlockMask being built")
+        num, idx, full = out.kv_num_blocks, out.kv_indices, out.kv_full
+    else:
+        num = torch.empty((B, 1, nqb), dtype=torch.int32, device=device)
+        idx = torch.empty((B, 1, nqb, nkb), dtype=torch.int32, device=device)
+        full = torch.empty((B, 1, nqb, nkb), dtype=torch.uint8, device=device) if with_full else None
     _need_device(num, idx, full, doc_ids)
     mk, mp = _mask_params(mask, window, prefix_len, doc_ids)
     rc = lib.attn_build_block_mask(mk, ctypes.byref(mp), B, Sq, Skv, q_block, kv_block,

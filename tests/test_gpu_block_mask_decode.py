@@ -315,3 +315,23 @@ def test_paged_decode_full_workload_window_alibi_sampled():
                                          mask=oracle.MaskSpec(oracle.MASK_SLIDING, window=1024))
         o_ref[i], l_ref[i] = o1[0], l1[0]
     compare(f64(out)[seqs], f64(lse)[seqs], o_ref, l_ref, torch.bfloat16, "paged decode full window")
+
+
+def test_block_mask_build_into_given_buffers():
+    """Building into an existing BlockMask's buffers overwrites every entry:
+    a document build over a causal one equals the oracle's document mask."""
+    dev = torch.device("cuda")
+    B, S = 2, 1000
+    doc = torch.from_numpy(_ids([100, 700, 37, 163], B))
+    announce("block mask build into given buffers")
+    bm = af.attn_build_block_mask("causal", B, S, S, device=dev)
+    out = af.attn_build_block_mask("document", B, S, S, doc_ids=doc.to(dev), device=dev, out=bm)
+    torch.cuda.synchronize()
+    assert out.kv_indices.data_ptr() == bm.kv_indices.data_ptr()
+    num, idx, full = oracle.block_mask_ref(oracle.MaskSpec(oracle.MASK_DOCUMENT, doc_ids=doc.numpy()),
+                                           B, S, S, 128, 128)
+    assert np.array_equal(out.kv_num_blocks.cpu().numpy(), num)
+    assert np.array_equal(out.kv_indices.cpu().numpy(), idx)
+    assert np.array_equal(out.kv_full.cpu().numpy(), full)
+    with pytest.raises(ValueError):
+        af.attn_build_block_mask("causal", B, S + 200, S + 200, device=dev, out=bm)

@@ -37,7 +37,8 @@
 // Tiles without a visible pair are skipped and the predicate is dropped on
 // tiles where every pair is visible, from the mask's closed-form bounds or,
 // given a BlockMask, from its lists: by query block for the dQ pass, by key
-// block for the dK/dV pass, staged in LDS.
+// block for the dK/dV pass, staged in LDS.  The tiles with the most work
+// launch first in both passes (with a BlockMask, ranked by list length).
 #include "kernels.h"
 
 namespace attn {

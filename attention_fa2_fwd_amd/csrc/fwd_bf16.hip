@@ -51,8 +51,9 @@
 //    index is permuted so that each XCD works on a contiguous run of heads,
 //    and the query heads of a GQA group read their K/V through one L2.
 //  * Causal-type masks: workgroups with the most key tiles are launched
-//    first; waves skip tiles that hold no visible key for their rows and
-//    skip the predicate on tiles where every key is visible.
+//    first (with a BlockMask, the query tiles with the most listed blocks);
+//    waves skip tiles that hold no visible key for their rows and skip the
+//    predicate on tiles where every key is visible.
 #include <type_traits>
 
 #include "kernels.h"

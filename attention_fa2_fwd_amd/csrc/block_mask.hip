@@ -78,28 +78,24 @@ __device__ __forceinline__ void document_block(const int32_t *doc_row, const int
     any = true;
     return;
   }
-  const int qval = qdoc[0];
-  int kmin, kmax;
-  bool k_uniform, hit_q = false;
   if (ksum) {
     // A shared id decides "any"; "all" needs one id on both sides.
     if (ksum->x > qmax || ksum->y < qmin || ksum->z == 0) return;
     any = true;
     all = q_uniform && ksum->x == ksum->y;
     return;
-  } else {
-    kmin = doc_row[k0];
-    kmax = kmin;
-    k_uniform = true;
-    for (int j = k0; j <= k1; ++j) {
-      const int d = doc_row[j];
-      kmin = min(kmin, d);
-      kmax = max(kmax, d);
-      k_uniform &= (d == kmin) && (d == kmax);
-      hit_q |= (d == qval);
-    }
-    if (kmax < qmin || kmin > qmax) return;
   }
+  const int qval = qdoc[0];
+  int kmin = doc_row[k0], kmax = kmin;
+  bool k_uniform = true, hit_q = false;
+  for (int j = k0; j <= k1; ++j) {
+    const int d = doc_row[j];
+    kmin = min(kmin, d);
+    kmax = max(kmax, d);
+    k_uniform &= (d == kmin) && (d == kmax);
+    hit_q |= (d == qval);
+  }
+  if (kmax < qmin || kmin > qmax) return;
   if (q_uniform) {
     any = hit_q;
     all = k_uniform && hit_q;

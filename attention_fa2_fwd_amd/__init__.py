@@ -11,6 +11,11 @@ Functions (same names as the C entry points):
     attn_build_block_mask(mask, B, Sq, Skv, ...) -> BlockMask
     attn_paged_decode_workspace_size(...)       -> int (bytes)
     attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, ...) -> (out, lse)
+    attn_block_mask_transpose(block_mask)       -> BlockMask with its lists by key block
+    attn_bwd(q, k, v, out, lse, dout, ...)      -> (dq, dk, dv)
+
+Every tensor's shape, dtype and device are checked against the sizes passed
+to the C ABI before any call (the library sees only pointers and sizes).
 """
 
 from __future__ import annotations
@@ -139,6 +144,63 @@ def _need_device(*tensors):
             raise ValueError("tensors must be contiguous device (GPU) tensors")
 
 
+def _expect(t, name: str, shape, dtypes=None):
+    """Refuse a tensor whose shape (or dtype) is not what the sizes passed to
+    the C ABI say: the library cannot see tensor sizes, so a short buffer would
+    be read or written out of bounds."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+
+
+def _same_device(ref, **named):
+    for name, t in named.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, not on {ref.device} with the other tensors")
+
+
+def _dims(t, name: str, n: int):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions (got shape {tuple(t.shape)})")
+
+
+def _check_block_mask(bm: BlockMask, B: int, Sq: int, Skv: int, ref, need_key_lists: bool):
+    _dims(bm.kv_indices, "block_mask.kv_indices", 4)
+    bb, one, nqb, nkb = bm.kv_indices.shape
+    if one != 1 or bb not in (1, B):
+        raise ValueError(f"block_mask.kv_indices has shape {tuple(bm.kv_indices.shape)}: "
+                         f"expected [1 or B={B}, 1, nQB, nKVB]")
+    if nqb != -(-Sq // bm.q_block) or nkb != -(-Skv // bm.kv_block):
+        raise ValueError(f"block_mask of {nqb} x {nkb} blocks of {bm.q_block} x {bm.kv_block} does "
+                         f"not cover Sq={Sq}, Skv={Skv}")
+    i32, u8 = (torch.int32,), (torch.uint8,)
+    _expect(bm.kv_num_blocks, "block_mask.kv_num_blocks", (bb, 1, nqb), i32)
+    _expect(bm.kv_indices, "block_mask.kv_indices", (bb, 1, nqb, nkb), i32)
+    _expect(bm.kv_full, "block_mask.kv_full", (bb, 1, nqb, nkb), u8)
+    if need_key_lists:
+        if bm.q_num_blocks is None or bm.q_indices is None:
+            raise ValueError("block_mask needs its lists by key block (attn_block_mask_transpose)")
+        _expect(bm.q_num_blocks, "block_mask.q_num_blocks", (bb, 1, nkb), i32)
+        _expect(bm.q_indices, "block_mask.q_indices", (bb, 1, nkb, nqb), i32)
+        _expect(bm.q_full, "block_mask.q_full", (bb, 1, nkb, nqb), u8)
+    _same_device(ref, kv_num_blocks=bm.kv_num_blocks, kv_indices=bm.kv_indices, kv_full=bm.kv_full,
+                 q_num_blocks=bm.q_num_blocks if need_key_lists else None,
+                 q_indices=bm.q_indices if need_key_lists else None,
+                 q_full=bm.q_full if need_key_lists else None)
+
+
+def _check_mask_score_tensors(mask: str, doc_ids, alibi_slopes, B: int, Skv: int, Hq: int, ref):
+    if doc_ids is not None:
+        _expect(doc_ids, "doc_ids", (B, Skv), (torch.int32,))
+    elif "document" in mask.split("&"):
+        raise ValueError("a document mask needs doc_ids [B, S]")
+    _expect(alibi_slopes, "alibi_slopes", (Hq,), (torch.float32,))
+    _same_device(ref, doc_ids=doc_ids, alibi_slopes=alibi_slopes)
+
+
 def _mask_params(mask: str, window: int, prefix_len: int, doc_ids: Optional[torch.Tensor]):
     kind, bits = _mask_kind(mask)
     if doc_ids is not None and doc_ids.dtype != torch.int32:
@@ -179,14 +241,22 @@ def attn_fwd(q, k, v, *, scale: Optional[float] = None, mask: str = "none", wind
     lib = load_library()
     if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype bf16 or float32")
+    _dims(q, "q", 4)
+    _dims(k, "k", 4)
     b, hq, sq, d = q.shape
     hkv, skv = k.shape[1], k.shape[2]
+    _expect(k, "k", (b, hkv, skv, d))
+    _expect(v, "v", (b, hkv, skv, d))
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
-    if out.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("out must be bf16 or float32")
     if lse is None:
         lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    _expect(out, "out", q.shape, (torch.bfloat16, torch.float32))
+    _expect(lse, "lse", (b, hq, sq), (torch.float32,))
+    _check_mask_score_tensors(mask, doc_ids, alibi_slopes, b, skv, hq, q)
+    _same_device(q, k=k, v=v, out=out, lse=lse)
+    if block_mask is not None:
+        _check_block_mask(block_mask, b, sq, skv, q, need_key_lists=False)
     _need_device(q, k, v, out, lse, doc_ids, alibi_slopes)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -221,6 +291,11 @@ def attn_build_block_mask(mask: str, B: int, Sq: int, Skv: int, *, q_block: int 
         num = torch.empty((B, 1, nqb), dtype=torch.int32, device=device)
         idx = torch.empty((B, 1, nqb, nkb), dtype=torch.int32, device=device)
         full = torch.empty((B, 1, nqb, nkb), dtype=torch.uint8, device=device) if with_full else None
+    _expect(num, "out.kv_num_blocks", (B, 1, nqb), (torch.int32,))
+    _expect(idx, "out.kv_indices", (B, 1, nqb, nkb), (torch.int32,))
+    _expect(full, "out.kv_full", (B, 1, nqb, nkb), (torch.uint8,))
+    _check_mask_score_tensors(mask, doc_ids, None, B, Skv, 0, idx)
+    _same_device(idx, kv_num_blocks=num, kv_full=full)
     _need_device(num, idx, full, doc_ids)
     mk, mp = _mask_params(mask, window, prefix_len, doc_ids)
     rc = lib.attn_build_block_mask(mk, ctypes.byref(mp), B, Sq, Skv, q_block, kv_block,
@@ -232,7 +307,9 @@ def attn_build_block_mask(mask: str, B: int, Sq: int, Skv: int, *, q_block: int 
 def attn_block_mask_transpose(bm: BlockMask) -> BlockMask:
     """The BlockMask with its lists by key block filled in (for attn_bwd)."""
     lib = load_library()
+    _dims(bm.kv_indices, "block_mask.kv_indices", 4)
     b, _, nqb, nkb = bm.kv_indices.shape
+    _check_block_mask(bm, b, nqb * bm.q_block, nkb * bm.kv_block, bm.kv_indices, need_key_lists=False)
     dev = bm.kv_indices.device
     qnum = torch.empty((b, 1, nkb), dtype=torch.int32, device=dev)
     qidx = torch.empty((b, 1, nkb, nqb), dtype=torch.int32, device=dev)
@@ -252,6 +329,47 @@ def attn_paged_decode_workspace_size(num_seqs: int, Hq: int, D: int, max_pages_p
                                                                 max_pages_per_seq, page_size))
 
 
+def _decode_args(q, k_cache, v_cache, page_table, seq_lens, scale, mask, window, score,
+                 alibi_slopes, rel_scale, softcap, out, lse):
+    """Checks shared by the two decode calls; returns the C arguments up to
+    the score params."""
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise ValueError("paged decode takes bf16 q and caches")
+    if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("page_table and seq_lens must be int32")
+    _dims(q, "q", 3)
+    _dims(k_cache, "k_cache", 4)
+    _dims(page_table, "page_table", 2)
+    n, hq, d = q.shape
+    pages, hkv, page_size, dc = k_cache.shape
+    if dc != d:
+        raise ValueError(f"k_cache rows hold {dc} values, q has D={d}")
+    _expect(v_cache, "v_cache", k_cache.shape)
+    if page_table.shape[0] != n:
+        raise ValueError(f"page_table has {page_table.shape[0]} rows for {n} sequences")
+    max_pages = page_table.shape[1]
+    _expect(seq_lens, "seq_lens", (n,))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+    _expect(out, "out", q.shape, (torch.bfloat16,))
+    _expect(lse, "lse", (n, hq), (torch.float32,))
+    _expect(alibi_slopes, "alibi_slopes", (hq,), (torch.float32,))
+    _same_device(q, k_cache=k_cache, v_cache=v_cache, page_table=page_table, seq_lens=seq_lens,
+                 out=out, lse=lse, alibi_slopes=alibi_slopes)
+    _need_device(q, k_cache, v_cache, page_table, seq_lens, out, lse, alibi_slopes)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sk, sp = _score_params(score, alibi_slopes, rel_scale, softcap)
+    mk, bits = _mask_kind(mask)
+    mp = MaskParams(int(window), 0, None, bits)
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), page_table.data_ptr(),
+            seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), BF16, n, hq, hkv, d, page_size,
+            max_pages, pages, float(scale), mk, mp, sk, sp)
+    return args, out, lse
+
+
 def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optional[float] = None,
                       mask: str = "none", window: int = 0, score: str = "none", alibi_slopes=None,
                       rel_scale: float = 1.0, softcap: float = 0.0, workspace=None, out=None,
@@ -261,32 +379,18 @@ def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optio
     "sliding" (the query at seq_lens-1 sees the last `window` keys).
     Returns (out, lse)."""
     lib = load_library()
-    n, hq, d = q.shape
-    pages, hkv, page_size, _ = k_cache.shape
-    max_pages = page_table.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+    args, out, lse = _decode_args(q, k_cache, v_cache, page_table, seq_lens, scale, mask, window,
+                                  score, alibi_slopes, rel_scale, softcap, out, lse)
+    n, hq, d, page_size, max_pages = args[8], args[9], args[11], args[12], args[13]
     need = attn_paged_decode_workspace_size(n, hq, d, max_pages, page_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise ValueError("page_table and seq_lens must be int32")
-    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
-        raise ValueError("paged decode takes bf16 q and caches")
-    _need_device(q, k_cache, v_cache, page_table, seq_lens, out, lse, workspace, alibi_slopes)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    sk, sp = _score_params(score, alibi_slopes, rel_scale, softcap)
-    mk, bits = _mask_kind(mask)
-    mp = MaskParams(int(window), 0, None, bits)
-    rc = lib.attn_paged_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                               page_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
-                               lse.data_ptr(), BF16, n, hq, hkv, d, page_size, max_pages, pages,
-                               float(scale), mk, ctypes.byref(mp), sk,
-                               ctypes.byref(sp), workspace.data_ptr(),
-                               workspace.numel() * workspace.element_size(), _stream(q.device))
+    _same_device(q, workspace=workspace)
+    _need_device(workspace)
+    mp, sp = args[17], args[19]
+    rc = lib.attn_paged_decode(*args[:17], ctypes.byref(mp), args[18], ctypes.byref(sp),
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream(q.device))
     _check("attn_paged_decode", rc)
     return out, lse
 
@@ -302,16 +406,28 @@ def attn_bwd(q, k, v, out, lse, dout, *, scale: Optional[float] = None, mask: st
     for t in (q, k, v, out, dout):
         if t.dtype != torch.bfloat16:
             raise ValueError("attn_bwd takes bf16 q, k, v, out, dout")
-    if lse.dtype != torch.float32:
-        raise ValueError("lse must be float32")
+    _dims(q, "q", 4)
+    _dims(k, "k", 4)
     b, hq, sq, d = q.shape
     hkv, skv = k.shape[1], k.shape[2]
+    _expect(k, "k", (b, hkv, skv, d))
+    _expect(v, "v", (b, hkv, skv, d))
+    _expect(out, "out", q.shape)
+    _expect(dout, "dout", q.shape)
+    _expect(lse, "lse", (b, hq, sq), (torch.float32,))
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    _expect(dq, "dq", q.shape, (torch.float32,))
+    _expect(dk, "dk", k.shape, (torch.float32,))
+    _expect(dv, "dv", k.shape, (torch.float32,))
+    _check_mask_score_tensors(mask, doc_ids, alibi_slopes, b, skv, hq, q)
     need = int(lib.attn_bwd_workspace_size(b, hq, sq))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _same_device(q, k=k, v=v, out=out, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    if block_mask is not None:
+        _check_block_mask(block_mask, b, sq, skv, q, need_key_lists=block_mask.q_indices is not None)
     _need_device(q, k, v, out, lse, dout, dq, dk, dv, workspace, doc_ids, alibi_slopes)
     if scale is None:
         scale = 1.0 / math.sqrt(d)

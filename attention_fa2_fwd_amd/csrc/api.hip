@@ -96,6 +96,71 @@ int launch_result(hipError_t e, const char *what) {
 
 }  // namespace
 
+namespace {
+
+// Validation shared by the two decode entry points; fills everything of p
+// but the workspace.  Returns ATTN_OK, an error, or 1 for an empty problem
+// (nothing to launch).
+int decode_prepare(const void *q, const void *k_cache, const void *v_cache, const int32_t *page_table,
+                   const int32_t *seq_lens, void *out, float *lse, attn_dtype_t dt, int N, int Hq,
+                   int Hkv, int D, int page_size, int max_pages_per_seq, int num_pages, float scale,
+                   attn_mask_kind_t mk, const attn_mask_params_t *mp, attn_score_kind_t sk,
+                   const attn_score_params_t *sp, attn::DecodeParams *p) {
+  if (N < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
+      num_pages < 0)
+    return fail(ATTN_ERR_INVALID, "bad size (N=%d Hq=%d Hkv=%d D=%d page=%d max_pages=%d pool=%d)",
+                N, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages);
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports bf16 only");
+  if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports D == 128 (got %d)", D);
+  if (page_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports page_size == 16");
+  if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports Hq/Hkv <= 16");
+  int rc = check_mask(mk, mp, 1, 1, &p->mask);
+  if (rc) return rc;
+  if (p->mask.kind != ATTN_MASK_NONE && p->mask.kind != ATTN_MASK_SLIDING)
+    return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports no mask or a sliding window");
+  rc = check_score(sk, sp, &p->score);
+  if (rc) return rc;
+  if (N == 0) {
+    g_err[0] = '\0';
+    return 1;
+  }
+  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out || !lse)
+    return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  p->q = q;
+  p->k_cache = k_cache;
+  p->v_cache = v_cache;
+  p->page_table = page_table;
+  p->seq_lens = seq_lens;
+  p->out = out;
+  p->lse = lse;
+  p->N = N;
+  p->Hq = Hq;
+  p->Hkv = Hkv;
+  p->D = D;
+  p->page_size = page_size;
+  p->max_pages = max_pages_per_seq;
+  p->num_pages = num_pages;
+  p->scale = scale;
+  return ATTN_OK;
+}
+
+// Bytes of split partials for `splits` splits per (sequence, query head):
+// fp32 rows of D, rounded up to 256 bytes, then one fp32 LSE per row.
+size_t decode_partials_bytes(int N, int Hq, int D, int splits) {
+  const size_t rows = (size_t)N * Hq * splits;
+  return (rows * D * sizeof(float) + 255) / 256 * 256 + rows * sizeof(float);
+}
+
+void decode_set_workspace(attn::DecodeParams *p, void *base, int splits) {
+  const size_t rows = (size_t)p->N * p->Hq * splits;
+  p->ws_o = (float *)base;
+  p->ws_lse = (float *)((char *)base + (rows * p->D * sizeof(float) + 255) / 256 * 256);
+  p->max_splits = splits;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *attn_last_error(void) { return g_err; }
@@ -217,52 +282,15 @@ int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
                       const attn_mask_params_t *mp, attn_score_kind_t sk,
                       const attn_score_params_t *sp, void *workspace, size_t workspace_bytes,
                       void *stream) {
-  if (N < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
-      num_pages < 0)
-    return fail(ATTN_ERR_INVALID, "bad size (N=%d Hq=%d Hkv=%d D=%d page=%d max_pages=%d pool=%d)",
-                N, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages);
-  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports bf16 only");
-  if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports D == 128 (got %d)", D);
-  if (page_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports page_size == 16");
-  if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports Hq/Hkv <= 16");
   attn::DecodeParams p{};
-  int rc = check_mask(mk, mp, 1, 1, &p.mask);
-  if (rc) return rc;
-  if (p.mask.kind != ATTN_MASK_NONE && p.mask.kind != ATTN_MASK_SLIDING)
-    return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports no mask or a sliding window");
-  rc = check_score(sk, sp, &p.score);
-  if (rc) return rc;
-  if (N == 0) {
-    g_err[0] = '\0';
-    return ATTN_OK;
-  }
-  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out || !lse)
-    return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  int rc = decode_prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, dt, N, Hq, Hkv, D,
+                          page_size, max_pages_per_seq, num_pages, scale, mk, mp, sk, sp, &p);
+  if (rc) return rc == 1 ? ATTN_OK : rc;
   const size_t need = attn_paged_decode_workspace_size(N, Hq, D, max_pages_per_seq, page_size);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   if (((uintptr_t)workspace) % 256 != 0) return fail(ATTN_ERR_INVALID, "workspace must be 256-byte aligned");
-  const int max_splits = attn::decode_max_splits(max_pages_per_seq);
-  const size_t rows = (size_t)N * Hq * max_splits;
-  p.q = q;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.page_table = page_table;
-  p.seq_lens = seq_lens;
-  p.out = out;
-  p.lse = lse;
-  p.N = N;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.D = D;
-  p.page_size = page_size;
-  p.max_pages = max_pages_per_seq;
-  p.num_pages = num_pages;
-  p.scale = scale;
-  p.ws_o = (float *)workspace;
-  p.ws_lse = (float *)((char *)workspace + (rows * D * sizeof(float) + 255) / 256 * 256);
-  p.max_splits = max_splits;
+  decode_set_workspace(&p, workspace, attn::decode_max_splits(max_pages_per_seq));
   return launch_result(attn::launch_paged_decode(p, (hipStream_t)stream), "attn_paged_decode");
 }
 

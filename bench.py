@@ -1,14 +1,16 @@
 #!/usr/bin/env python3
 """Throughput of the gfx950 attention path on one MI355X.
 
-A step is one pass of the headline prefill workload: bf16 B=4, Hq=Hkv=16,
-S=2048, D=64, run once with no mask and once causal (two attn_fwd launches on
-inputs already resident in HBM).  The JSON line reports unmasked TFLOP/s
-(4*D FLOPs per visible (query, key) pair) and the fraction of the 2.5 PFLOP/s
-dense bf16 MFMA peak, the forward kernel's own launch times from HIP events,
-the CPU oracle timed on a bounded sample of the same workload, and per-workload
-figures for the other prefill shapes, the BlockMask build and the paged decode
-(HBM GB/s against 8 TB/s).
+A step is one attn_fwd launch on the headline workload, the largest
+single-GPU prefill configuration: bf16 GQA sliding window 1024 + ALiBi,
+B=2, Hq=32, Hkv=8, S=8192, D=128, seed 0, inputs already resident in HBM.
+The JSON line reports unmasked TFLOP/s (4*D FLOPs per visible (query, key)
+pair) against the 2.5 PFLOP/s dense bf16 MFMA peak, with the forward kernel's
+launch times (mean, median, min) from HIP events on the launch stream; a
+second roofline block for the paged decode of 64 sequences (HBM bytes
+against 8 TB/s); the CPU oracle timed on (batch, head) slices of the
+benchmarked tensors; and per-workload figures for the other prefill shapes,
+the BlockMask build, the backward and the decode.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
                        [--no-cpu-baseline] [--only WORKLOAD] [--mode copy]
@@ -70,21 +72,29 @@ def load_traffic(kernel_src: str, key: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-class Timer:
-    """HIP events on torch's current stream (the stream the kernels run on)."""
+def time_launches(torch, fn, steps: int):
+    """Run fn `steps` times back to back with a HIP event recorded on the
+    launch stream (torch's current stream, where the binding enqueues) before
+    the first launch and after each one.  Returns the mean over the whole
+    run and the median and min of the per-launch intervals, in ms."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    mid = steps // 2
+    median = per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return {"mean_ms": evs[0].elapsed_time(evs[steps]) / steps, "median_ms": median, "min_ms": per[0]}
 
-    def __init__(self, torch):
-        self.torch = torch
 
-    def event(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-
-def bench_prefill(af, torch, workloads, w, steps, warmup, out_dtype=None, with_block_mask=None):
+def bench_prefill(af, torch, workloads, w, steps, warmup, out_dtype=None, with_block_mask=None,
+                  inputs=None):
+    """attn_fwd on a prefill workload; the BlockMask (when the workload has
+    one) is built once, timed on its own and reused by every launch."""
     dev = torch.device("cuda")
-    inp = workloads.prefill_inputs(w)
+    inp = workloads.prefill_inputs(w) if inputs is None else inputs
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     doc = inp["doc_ids"].to(dev) if inp["doc_ids"] is not None else None
     use_bm = w.block_mask if with_block_mask is None else with_block_mask
@@ -97,13 +107,10 @@ def bench_prefill(af, torch, workloads, w, steps, warmup, out_dtype=None, with_b
         torch.cuda.synchronize()
         # Builds into the same buffers, so the host issues them faster than
         # the kernel runs and the events time the kernels.
-        e0 = Timer(torch).event()
-        for _ in range(10):
-            af.attn_build_block_mask(w.mask, w.B, w.Sq, w.Skv, window=w.window,
-                                     prefix_len=w.prefix_len, doc_ids=doc, device=dev, out=bm)
-        e1 = Timer(torch).event()
-        torch.cuda.synchronize()
-        bm_us = e0.elapsed_time(e1) * 1000.0 / 10
+        t_bm = time_launches(torch, lambda: af.attn_build_block_mask(
+            w.mask, w.B, w.Sq, w.Skv, window=w.window, prefix_len=w.prefix_len, doc_ids=doc,
+            device=dev, out=bm), 10)
+        bm_us = t_bm["mean_ms"] * 1000.0
     out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     kw = dict(scale=1.0 / math.sqrt(w.D), mask=w.mask, window=w.window, prefix_len=w.prefix_len,
@@ -111,16 +118,12 @@ def bench_prefill(af, torch, workloads, w, steps, warmup, out_dtype=None, with_b
     for _ in range(warmup):
         af.attn_fwd(q, k, v, **kw)
     torch.cuda.synchronize()
-    t = Timer(torch)
-    e0 = t.event()
-    for _ in range(steps):
-        af.attn_fwd(q, k, v, **kw)
-    e1 = t.event()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    t = time_launches(torch, lambda: af.attn_fwd(q, k, v, **kw), steps)
     pairs = visible_pairs(w.mask, w.Sq, w.window, inp["doc_lengths"])
     flops = 4.0 * w.D * w.B * w.Hq * pairs
-    res = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "gflop": flops / 1e9}
+    ms = t["mean_ms"]
+    res = {"ms": ms, "median_ms": t["median_ms"], "min_ms": t["min_ms"],
+           "tflops": flops / (ms * 1e-3) / 1e12, "gflop": flops / 1e9}
     res["frac_mfma_peak"] = res["tflops"] / MFMA_PEAK_TFLOPS
     if bm_us is not None:
         res["block_mask_build_us"] = bm_us
@@ -154,17 +157,26 @@ def bench_backward(af, torch, workloads, w, steps, warmup):
     for _ in range(warmup):
         af.attn_bwd(q, k, v, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
     torch.cuda.synchronize()
-    t = Timer(torch)
-    e0 = t.event()
-    for _ in range(steps):
-        af.attn_bwd(q, k, v, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
-    e1 = t.event()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    t = time_launches(torch, lambda: af.attn_bwd(q, k, v, out, lse, do, dq=dq, dk=dk, dv=dv,
+                                                 workspace=ws, **kw), steps)
+    ms = t["mean_ms"]
     pairs = visible_pairs(w.mask, w.Sq, w.window, inp["doc_lengths"])
     flops = 10.0 * w.D * w.B * w.Hq * pairs
     tf = flops / (ms * 1e-3) / 1e12
-    return {"ms": ms, "tflops": tf, "gflop": flops / 1e9, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS}
+    return {"ms": ms, "median_ms": t["median_ms"], "min_ms": t["min_ms"], "tflops": tf,
+            "gflop": flops / 1e9, "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS}
+
+
+def decode_algorithmic_bytes(w, lengths, window=0, hq=None):
+    """Bytes the decode must move: each valid K/V byte once (per kv head),
+    plus Q, O, LSE, the page ids of the pages read and seq_lens."""
+    hq = w.Hq if hq is None else hq
+    n = len(lengths)
+    first = [max(0, L - window) if window else 0 for L in lengths]
+    tokens = sum(L - t0 for L, t0 in zip(lengths, first))
+    kv_bytes = tokens * 2 * w.Hkv * w.D * 2
+    pages = sum(-(-L // w.page_size) - t0 // w.page_size for L, t0 in zip(lengths, first))
+    return kv_bytes + n * hq * w.D * 2 * 2 + n * hq * 4 + pages * 4 + n * 4, tokens
 
 
 def bench_decode(af, torch, workloads, steps, warmup, window=0, score="none"):
@@ -184,54 +196,81 @@ def bench_decode(af, torch, workloads, steps, warmup, window=0, score="none"):
     for _ in range(warmup):
         af.attn_paged_decode(*args, **kw)
     torch.cuda.synchronize()
-    t = Timer(torch)
-    e0 = t.event()
-    for _ in range(steps):
-        af.attn_paged_decode(*args, **kw)
-    e1 = t.event()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    t = time_launches(torch, lambda: af.attn_paged_decode(*args, **kw), steps)
+    ms = t["mean_ms"]
     lengths = [int(L) for L in inp["lengths"]]
-    first = [max(0, L - window) if window else 0 for L in lengths]
-    tokens = sum(L - t0 for L, t0 in zip(lengths, first))
-    kv_bytes = tokens * 2 * w.Hkv * w.D * 2
-    pages = sum(-(-L // w.page_size) - t0 // w.page_size for L, t0 in zip(lengths, first))
-    algo_bytes = kv_bytes + n * hq * d * 2 * 2 + n * hq * 4 + pages * 4 + n * 4
+    algo_bytes, tokens = decode_algorithmic_bytes(w, lengths, window)
     gbs = algo_bytes / (ms * 1e-3) / 1e9
-    return {"ms": ms, "GB_per_s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
-            "algorithmic_bytes": algo_bytes, "tokens": tokens}
+    return {"ms": ms, "median_ms": t["median_ms"], "min_ms": t["min_ms"], "GB_per_s": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS, "algorithmic_bytes": algo_bytes, "tokens": tokens}
 
 
-def cpu_baseline(workloads, budget_s: float = 12.0):
-    """The oracle, as it stands, on whole (batch, head) slices of the headline
-    workload until about budget_s of CPU time is spent; rate on the same
-    unmasked-FLOP basis."""
+def host_info():
+    """CPU model, BLAS library and NumPy version of this host, and the BLAS
+    thread count NumPy runs with."""
     import numpy as np
-    import oracle
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", os.cpu_count() or 1
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            blas = f"{infos[0].get('internal_api')} {infos[0].get('version')}"
+            threads = max(int(i.get("num_threads", 1)) for i in infos)
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    w_dense, w_causal = workloads.DENSE_BF16, workloads.CAUSAL_BF16
-    q, k, v = workloads.randn_qkv(1, 1, 1, w_dense.Sq, w_dense.Skv, w_dense.D, "bf16", 0)
-    qf = q.float().numpy().astype(np.float64)
-    kf = k.float().numpy().astype(np.float64)
-    vf = v.float().numpy().astype(np.float64)
-    scale = 1.0 / math.sqrt(w_dense.D)
+        pass
+    return {"cpu_model": model, "blas": blas, "numpy": np.__version__, "threads": int(threads)}
+
+
+def cpu_baseline(workloads, w, q, k, v, budget_s: float = 15.0):
+    """The oracle, as it stands, on whole (batch, head) slices of the
+    benchmarked tensors (the same bf16 values, read back as float64) until
+    about budget_s of wall-clock time is spent; rate on the same
+    unmasked-FLOP basis as the GPU figure (the oracle does the dense S x S
+    work whatever the mask, so the rate is low by construction)."""
+    import numpy as np
+    import oracle
+    info = host_info()
+    scale = 1.0 / math.sqrt(w.D)
+    ms = oracle.MaskSpec(workloads.MASK_NAMES[w.mask], window=w.window, prefix_len=w.prefix_len)
+    ss = oracle.ScoreSpec(workloads.SCORE_NAMES[w.score])
+    pairs = visible_pairs(w.mask, w.Sq, w.window)
+    slices = []
     flops = 0.0
-    slices = 0
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        oracle.attention_ref(qf, kf, vf, scale, oracle.MaskSpec(oracle.MASK_NONE))
-        oracle.attention_ref(qf, kf, vf, scale, oracle.MaskSpec(oracle.MASK_CAUSAL))
-        S = w_dense.Sq
-        flops += 4.0 * w_dense.D * (S * S + S * (S + 1) // 2)
-        slices += 1
+    for b in range(w.B):
+        for hq in range(w.Hq):
+            if time.perf_counter() - t0 >= budget_s:
+                break
+            hkv = hq * w.Hkv // w.Hq
+            qs = q[b, hq].float().cpu().numpy().astype(np.float64)
+            ks = k[b, hkv].float().cpu().numpy().astype(np.float64)
+            vs = v[b, hkv].float().cpu().numpy().astype(np.float64)
+            for r0 in range(0, w.Sq, 1024):
+                rows = np.arange(r0, min(w.Sq, r0 + 1024))
+                oracle.attention_rows(qs[rows], ks, vs, rows, b, hq, w.Hq, scale, ms, ss)
+            flops += 4.0 * w.D * pairs
+            slices.append((b, hq))
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{slices} x (one (batch, head) slice dense + one causal) of the "
-                      f"B=4 H=16 S=2048 D=64 workload, float64 NumPy, {dt:.1f} s"}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": info["threads"], "kind": "oracle",
+            "sample": f"{len(slices)} (batch, head) slices {slices[0]}..{slices[-1]} of the benchmarked "
+                      f"{w.name} tensors, each its full {w.Sq} query rows against its kv head, "
+                      f"float64 NumPy, {dt:.1f} s wall-clock (including the slices' host copies)",
+            "seconds": round(dt, 3), "cpu_model": info["cpu_model"], "blas": info["blas"],
+            "numpy": info["numpy"]}
+
+
+ONLY = ("dense, causal, gqa, document, causal_softcap, document_window, decode, decode_window, "
+        "bwd_causal, bwd_dense, bwd_gqa, bwd_document; for scale: long_dense_d128, "
+        "long_causal_d128, long_dense_d64")
 
 
 def main():
@@ -241,11 +280,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default=None,
-                    help="run one workload (dense, causal, gqa, document, causal_softcap, "
-                         "document_window, decode, decode_window, bwd_causal, bwd_dense, "
-                         "bwd_gqa, bwd_document; for scale: long_dense_d128, "
-                         "long_causal_d128, long_dense_d64) and exit")
+    ap.add_argument("--only", default=None, help=f"run one workload ({ONLY}) and exit")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy, to calibrate byte counters")
     args = ap.parse_args()
@@ -288,69 +323,39 @@ def main():
                   "bwd_dense": workloads.DENSE_BF16,
                   "bwd_document": workloads.DOCUMENT_BLOCKMASK}[args.only]
             r = bench_backward(af, torch, workloads, wl, args.steps, args.warmup)
-            print(json.dumps({"workload": args.only, **r}), flush=True)
-            return
-        if args.only == "decode":
+        elif args.only == "decode":
             r = bench_decode(af, torch, workloads, args.steps, args.warmup)
         elif args.only == "decode_window":
             r = bench_decode(af, torch, workloads, args.steps, args.warmup, window=1024, score="alibi")
-        else:
+        elif args.only in sel:
             r = bench_prefill(af, torch, workloads, sel[args.only], args.steps, args.warmup)
+        else:
+            ap.error(f"--only takes one of: {ONLY}")
         print(json.dumps({"workload": args.only, **r}), flush=True)
         return
 
-    # ---- headline: dense + causal prefill, bf16 B=4 H=16 S=2048 D=64
+    # ---- headline: GQA sliding window 1024 + ALiBi, bf16 B=2 Hq=32 Hkv=8 S=8192 D=128
     dev = torch.device("cuda")
-    wd, wc = workloads.DENSE_BF16, workloads.CAUSAL_BF16
-    q, k, v = workloads.randn_qkv(wd.B, wd.Hq, wd.Hkv, wd.Sq, wd.Skv, wd.D, "bf16", 0)
-    q, k, v = q.to(dev), k.to(dev), v.to(dev)
-    out_d = torch.empty_like(q)
-    out_c = torch.empty_like(q)
-    lse_d = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    lse_c = torch.empty_like(lse_d)
-    scale = 1.0 / math.sqrt(wd.D)
+    w = workloads.GQA_WINDOW_ALIBI
+    inp = workloads.prefill_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(w.D)
 
-    def dense():
-        af.attn_fwd(q, k, v, scale=scale, mask="none", out=out_d, lse=lse_d)
-
-    def causal():
-        af.attn_fwd(q, k, v, scale=scale, mask="causal", out=out_c, lse=lse_c)
+    def step():
+        af.attn_fwd(q, k, v, scale=scale, mask=w.mask, window=w.window, score=w.score, out=out, lse=lse)
 
     for _ in range(args.warmup):
-        dense()
-        causal()
+        step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-    t = Timer(torch)
-    e0 = t.event()
-    for _ in range(args.steps):
-        dense()
-        causal()
-    e1 = t.event()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-
-    # Launch duration of each kernel variant: the same launch back to back
-    # between two events on the launch stream, so the figure is the kernel's
-    # own time (the launches queue ahead of the GPU).
-    def launch_ms(fn):
-        a0 = t.event()
-        for _ in range(args.steps):
-            fn()
-        a1 = t.event()
-        torch.cuda.synchronize()
-        return a0.elapsed_time(a1) / args.steps
-
-    dense_ms = launch_ms(dense)
-    causal_ms = launch_ms(causal)
-    S = wd.Sq
-    f_dense = 4.0 * wd.D * wd.B * wd.Hq * S * S
-    f_causal = 4.0 * wd.D * wd.B * wd.Hq * S * (S + 1) // 2
-    value = (f_dense + f_causal) / (ms_step * 1e-3) / 1e12
-    kernel_ms = (dense_ms + causal_ms) / 2.0                     # mean launch duration
-    achieved = ((f_dense + f_causal) / 2.0) / (kernel_ms * 1e-3) / 1e12
+    t = time_launches(torch, step, args.steps)     # synchronised on both sides
+    ms_step = t["mean_ms"]
+    pairs = visible_pairs(w.mask, w.Sq, w.window)
+    flops = 4.0 * w.D * w.B * w.Hq * pairs
+    value = flops / (ms_step * 1e-3) / 1e12
     src = os.path.join(ROOT, "attention_fa2_fwd_amd", "csrc", "fwd_bf16.hip")
-    traffic = load_traffic(src, "fwd_bf16_d64_dense_causal")
     print(f"[bench] headline done: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
     line = {
@@ -366,44 +371,60 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "dense_and_causal_prefill_bf16_b4_h16_s2048_d64",
-                   "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "S": S, "D": wd.D,
-                   "masks": ["none", "causal"], "out_dtype": "bf16",
-                   "flop_basis": "4*D per visible (query, key) pair"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "fwd_bf16_kernel<64, bf16 out>",
-                     "launch_ms": {"dense": round(dense_ms, 5), "causal": round(causal_ms, 5)}},
+        "config": {"workload": "gqa_sliding_window1024_alibi_prefill_bf16_b2_hq32_hkv8_s8192_d128",
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.Sq, "D": w.D, "mask": "sliding",
+                   "window": w.window, "score": "alibi", "seed": w.seed, "out_dtype": "bf16",
+                   "flop_basis": "4*D per visible (query, key) pair",
+                   "visible_pairs_per_head": pairs},
+        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(value / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic(src, "fwd_bf16_d128_gqa_window1024_alibi"),
+                     "kernel": "fwd_bf16_kernel<128, SLIDING, bias, bf16 out>",
+                     "flop_per_launch": flops,
+                     "launch_ms": {"mean": round(t["mean_ms"], 5), "median": round(t["median_ms"], 5),
+                                   "min": round(t["min_ms"], 5)},
+                     "tflops_at_median": round(flops / (t["median_ms"] * 1e-3) / 1e12, 3)},
         "cpu_baseline": None,
     }
 
+    # ---- paged decode roofline (HBM), 64 sequences
+    print("[bench] paged decode", file=sys.stderr, flush=True)
+    dec = bench_decode(af, torch, workloads, 20, 3)
+    dsrc = os.path.join(ROOT, "attention_fa2_fwd_amd", "csrc", "decode.hip")
+    line["roofline_decode"] = {
+        "bound": "hbm", "achieved": round(dec["GB_per_s"], 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(dec["frac_hbm_peak"], 4),
+        "traffic": load_traffic(dsrc, "paged_decode_64seq"),
+        "kernel": "decode_split_kernel + decode_combine_kernel (one attn_paged_decode call)",
+        "workload": "paged_gqa_decode_bf16_n64_hq32_hkv8_d128_page16",
+        "bytes_per_call": dec["algorithmic_bytes"],
+        "call_ms": {"mean": round(dec["ms"], 5), "median": round(dec["median_ms"], 5),
+                    "min": round(dec["min_ms"], 5)}}
+
     if not args.no_extra:
         extra = {}
-        for name, w in (("gqa_window1024_alibi", workloads.GQA_WINDOW_ALIBI),
-                        ("document_blockmask", workloads.DOCUMENT_BLOCKMASK),
-                        ("causal_softcap5", workloads.CAUSAL_SOFTCAP),
-                        ("document_window1024_blockmask", workloads.DOC_WINDOW_BLOCKMASK)):
+        for name, wl in (("dense_b4h16s2048d64", workloads.DENSE_BF16),
+                         ("causal_b4h16s2048d64", workloads.CAUSAL_BF16),
+                         ("document_blockmask", workloads.DOCUMENT_BLOCKMASK),
+                         ("causal_softcap5", workloads.CAUSAL_SOFTCAP),
+                         ("document_window1024_blockmask", workloads.DOC_WINDOW_BLOCKMASK)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
-            extra[name] = bench_prefill(af, torch, workloads, w, 20, 3)
-        for name, w in (("backward_causal_b4h16s2048d64", workloads.CAUSAL_BF16),
-                        ("backward_gqa_window1024_alibi", workloads.GQA_WINDOW_ALIBI),
-                        ("backward_document_blockmask", workloads.DOCUMENT_BLOCKMASK)):
+            extra[name] = bench_prefill(af, torch, workloads, wl, 20, 3)
+        for name, wl in (("backward_causal_b4h16s2048d64", workloads.CAUSAL_BF16),
+                         ("backward_gqa_window1024_alibi", workloads.GQA_WINDOW_ALIBI),
+                         ("backward_document_blockmask", workloads.DOCUMENT_BLOCKMASK)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
-            extra[name] = bench_backward(af, torch, workloads, w, 10, 2)
-        print("[bench] paged decode", file=sys.stderr, flush=True)
-        extra["paged_decode"] = bench_decode(af, torch, workloads, 20, 3)
+            extra[name] = bench_backward(af, torch, workloads, wl, 10, 2)
+        extra["paged_decode"] = dec
         print("[bench] paged decode, window 1024 + alibi", file=sys.stderr, flush=True)
         extra["paged_decode_window1024_alibi"] = bench_decode(af, torch, workloads, 20, 3,
                                                               window=1024, score="alibi")
         line["workloads"] = {k2: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                                   for kk, vv in r.items()} for k2, r in extra.items()}
-        line["workloads"]["dense_causal_split"] = {
-            "dense_tflops": round(f_dense / (dense_ms * 1e-3) / 1e12, 3),
-            "causal_tflops": round(f_causal / (causal_ms * 1e-3) / 1e12, 3)}
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(workloads)
+        line["cpu_baseline"] = cpu_baseline(workloads, w, q, k, v)
     print(json.dumps(line), flush=True)
 
 

@@ -183,3 +183,115 @@ def test_block_mask_transpose_checks():
     assert lib.attn_block_mask_transpose(ctypes.byref(bm), None, None, None, None) == -1
     empty = af.BlockMaskC(None, None, None, 128, 128, 2, 0, 1, None, None, None)
     assert lib.attn_block_mask_transpose(ctypes.byref(empty), None, None, None, None) == 0
+
+
+# ---- the binding refuses tensors that do not match the sizes it passes to C
+# (CPU tensors: every shape check runs before the device check, so a refusal
+# here names the shape, and a consistent call gets as far as the device check)
+
+import torch  # noqa: E402
+
+
+def _qkv(B=1, Hq=4, Hkv=2, S=32, D=64, dt=torch.bfloat16):
+    return (torch.zeros(B, Hq, S, D, dtype=dt), torch.zeros(B, Hkv, S, D, dtype=dt),
+            torch.zeros(B, Hkv, S, D, dtype=dt))
+
+
+@pytest.mark.parametrize("change,what", [
+    (dict(out=torch.zeros(1, 4, 31, 64, dtype=torch.bfloat16)), "out"),
+    (dict(lse=torch.zeros(1, 4, 16)), "lse"),
+    (dict(lse=torch.zeros(1, 4, 32, dtype=torch.float64)), "lse"),
+    (dict(k=torch.zeros(2, 2, 32, 64, dtype=torch.bfloat16)), "k"),
+    (dict(k=torch.zeros(1, 2, 32, 128, dtype=torch.bfloat16)), "k"),
+    (dict(v=torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)), "v"),
+    (dict(mask="document", doc_ids=torch.zeros(1, 16, dtype=torch.int32)), "doc_ids"),
+    (dict(mask="document"), "doc_ids"),
+    (dict(score="alibi", alibi_slopes=torch.zeros(3)), "alibi_slopes"),
+])
+def test_binding_fwd_refuses_mismatched_tensors(change, what):
+    q, k, v = _qkv()
+    kw = dict(change)
+    k = kw.pop("k", k)
+    v = kw.pop("v", v)
+    with pytest.raises(ValueError, match=what):
+        af.attn_fwd(q, k, v, **kw)
+
+
+def test_binding_fwd_block_mask_shapes_and_device_check_last():
+    q, k, v = _qkv(S=300)
+    num = torch.zeros(1, 1, 3, dtype=torch.int32)
+    idx = torch.zeros(1, 1, 3, 3, dtype=torch.int32)
+    full = torch.zeros(1, 1, 3, 3, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="kv_num_blocks"):
+        af.attn_fwd(q, k, v, block_mask=af.BlockMask(torch.zeros(1, 1, 2, dtype=torch.int32), idx, full,
+                                                     128, 128))
+    with pytest.raises(ValueError, match="kv_full"):
+        af.attn_fwd(q, k, v, block_mask=af.BlockMask(num, idx, torch.zeros(1, 1, 3, 2, dtype=torch.uint8),
+                                                     128, 128))
+    with pytest.raises(ValueError, match="does not cover"):
+        af.attn_fwd(q, k, v, block_mask=af.BlockMask(num[:, :, :2], idx[:, :, :2], None, 128, 128))
+    with pytest.raises(ValueError, match="expected \\[1 or B"):
+        af.attn_fwd(q, k, v, block_mask=af.BlockMask(num.expand(3, 1, 3).contiguous(),
+                                                     idx.expand(3, 1, 3, 3).contiguous(), None, 128, 128))
+    # consistent shapes: refused only because the tensors are not on a GPU
+    with pytest.raises(ValueError, match="device"):
+        af.attn_fwd(q, k, v, block_mask=af.BlockMask(num, idx, full, 128, 128))
+
+
+def _dec_inputs(N=3, Hq=8, Hkv=2, D=128, pages=10, max_pages=4):
+    return (torch.zeros(N, Hq, D, dtype=torch.bfloat16),
+            torch.zeros(pages, Hkv, 16, D, dtype=torch.bfloat16),
+            torch.zeros(pages, Hkv, 16, D, dtype=torch.bfloat16),
+            torch.zeros(N, max_pages, dtype=torch.int32), torch.zeros(N, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("fn", ["attn_paged_decode"])
+@pytest.mark.parametrize("change,what", [
+    (dict(page_table=torch.zeros(2, 4, dtype=torch.int32)), "page_table"),
+    (dict(seq_lens=torch.zeros(4, dtype=torch.int32)), "seq_lens"),
+    (dict(out=torch.zeros(3, 8, 64, dtype=torch.bfloat16)), "out"),
+    (dict(lse=torch.zeros(3, 4)), "lse"),
+    (dict(v_cache=torch.zeros(9, 2, 16, 128, dtype=torch.bfloat16)), "v_cache"),
+    (dict(k_cache=torch.zeros(10, 2, 16, 64, dtype=torch.bfloat16),
+          v_cache=torch.zeros(10, 2, 16, 64, dtype=torch.bfloat16)), "k_cache"),
+    (dict(alibi_slopes=torch.zeros(4)), "alibi_slopes"),
+    (dict(), "device"),
+])
+def test_binding_decode_refuses_mismatched_tensors(fn, change, what):
+    q, kc, vc, table, lens = _dec_inputs()
+    kw = dict(change)
+    q = kw.pop("q", q)
+    kc = kw.pop("k_cache", kc)
+    vc = kw.pop("v_cache", vc)
+    table = kw.pop("page_table", table)
+    lens = kw.pop("seq_lens", lens)
+    with pytest.raises(ValueError, match=what):
+        getattr(af, fn)(q, kc, vc, table, lens, **kw)
+
+
+@pytest.mark.parametrize("change,what", [
+    (dict(dq=torch.zeros(1, 4, 32, 64, dtype=torch.bfloat16)), "dq"),
+    (dict(dk=torch.zeros(1, 4, 32, 64)), "dk"),
+    (dict(dv=torch.zeros(1, 2, 31, 64)), "dv"),
+    (dict(lse=torch.zeros(1, 4, 31)), "lse"),
+    (dict(out=torch.zeros(1, 4, 31, 64, dtype=torch.bfloat16)), "out"),
+    (dict(dout=torch.zeros(1, 4, 32, 128, dtype=torch.bfloat16)), "dout"),
+    (dict(mask="document", doc_ids=torch.zeros(2, 32, dtype=torch.int32)), "doc_ids"),
+    (dict(), "device"),
+])
+def test_binding_bwd_refuses_mismatched_tensors(change, what):
+    q, k, v = _qkv()
+    kw = dict(change)
+    out = kw.pop("out", torch.zeros_like(q))
+    dout = kw.pop("dout", torch.zeros_like(q))
+    lse = kw.pop("lse", torch.zeros(1, 4, 32))
+    with pytest.raises(ValueError, match=what):
+        af.attn_bwd(q, k, v, out, lse, dout, **kw)
+
+
+def test_binding_build_block_mask_refuses_short_doc_ids():
+    with pytest.raises(ValueError, match="doc_ids"):
+        af.attn_build_block_mask("document", 1, 300, 300, doc_ids=torch.zeros(1, 200, dtype=torch.int32),
+                                 device="cpu")
+    with pytest.raises(ValueError, match="doc_ids"):
+        af.attn_build_block_mask("document", 1, 300, 300, device="cpu")

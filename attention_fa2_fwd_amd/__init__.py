@@ -11,6 +11,7 @@ Functions (same names as the C entry points):
     attn_build_block_mask(mask, B, Sq, Skv, ...) -> BlockMask
     attn_paged_decode_workspace_size(...)       -> int (bytes)
     attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, ...) -> (out, lse)
+    attn_paged_decode_noalloc(q, k_cache, v_cache, page_table, seq_lens, ...) -> (out, lse)
     attn_block_mask_transpose(block_mask)       -> BlockMask with its lists by key block
     attn_bwd(q, k, v, out, lse, dout, ...)      -> (dq, dk, dv)
 
@@ -37,7 +38,7 @@ MASK_AND = 5   # masks joined with "&", e.g. "sliding&document&causal"
 SCORE_KINDS = {"none": 0, "alibi": 1, "rel_pos": 2, "softcap": 3}
 EXPORTED = ("attn_fwd", "attn_build_block_mask", "attn_block_mask_transpose",
             "attn_paged_decode_workspace_size", "attn_paged_decode", "attn_bwd_workspace_size",
-            "attn_bwd", "attn_last_error")
+            "attn_bwd", "attn_paged_decode_noalloc", "attn_last_error")
 
 
 class AttnError(RuntimeError):
@@ -110,6 +111,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       i32, i32, f32, i32, ctypes.POINTER(MaskParams), i32,
                                       ctypes.POINTER(ScoreParams), vp, ctypes.c_size_t, vp]
     lib.attn_paged_decode.restype = i32
+    lib.attn_paged_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                              i32, i32, f32, i32, ctypes.POINTER(MaskParams), i32,
+                                              ctypes.POINTER(ScoreParams), vp]
+    lib.attn_paged_decode_noalloc.restype = i32
     lib.attn_block_mask_transpose.argtypes = [ctypes.POINTER(BlockMaskC), vp, vp, vp, vp]
     lib.attn_block_mask_transpose.restype = i32
     lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
@@ -392,6 +397,24 @@ def attn_paged_decode(q, k_cache, v_cache, page_table, seq_lens, *, scale: Optio
                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                _stream(q.device))
     _check("attn_paged_decode", rc)
+    return out, lse
+
+
+def attn_paged_decode_noalloc(q, k_cache, v_cache, page_table, seq_lens, *,
+                              scale: Optional[float] = None, mask: str = "none", window: int = 0,
+                              score: str = "none", alibi_slopes=None, rel_scale: float = 1.0,
+                              softcap: float = 0.0, out=None, lse=None):
+    """attn_paged_decode without a workspace: the split partials go to the
+    library's fixed per-GPU scratch (64 MiB), so the C call allocates
+    nothing (pass out and lse to allocate nothing here either).  Calls that
+    overlap on one GPU race for that scratch."""
+    lib = load_library()
+    args, out, lse = _decode_args(q, k_cache, v_cache, page_table, seq_lens, scale, mask, window,
+                                  score, alibi_slopes, rel_scale, softcap, out, lse)
+    mp, sp = args[17], args[19]
+    rc = lib.attn_paged_decode_noalloc(*args[:17], ctypes.byref(mp), args[18], ctypes.byref(sp),
+                                       _stream(q.device))
+    _check("attn_paged_decode_noalloc", rc)
     return out, lse
 
 

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -159,6 +160,44 @@ void decode_set_workspace(attn::DecodeParams *p, void *base, int splits) {
   p->max_splits = splits;
 }
 
+// Scratch of attn_paged_decode_noalloc, for callers that cannot allocate:
+// one array per GPU, held for the life of the process.  Host code never
+// takes the array's own address (on the host it is only a stand-in for the
+// symbol); it uses the device address hipGetSymbolAddress returns, looked up
+// once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (the device the stream belongs to,
+// which must be the current one).
+int scratch_address(hipStream_t stream, void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(ATTN_ERR_INVALID, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(ATTN_ERR_INVALID, "the stream belongs to device %d but device %d is current", (int)sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !addr)
+      return fail(ATTN_ERR_LAUNCH, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = addr;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -292,6 +331,32 @@ int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
   if (((uintptr_t)workspace) % 256 != 0) return fail(ATTN_ERR_INVALID, "workspace must be 256-byte aligned");
   decode_set_workspace(&p, workspace, attn::decode_max_splits(max_pages_per_seq));
   return launch_result(attn::launch_paged_decode(p, (hipStream_t)stream), "attn_paged_decode");
+}
+
+int attn_paged_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *page_table, const int32_t *seq_lens, void *out, float *lse,
+                              attn_dtype_t dt, int N, int Hq, int Hkv, int D, int page_size,
+                              int max_pages_per_seq, int num_pages, float scale, attn_mask_kind_t mk,
+                              const attn_mask_params_t *mp, attn_score_kind_t sk,
+                              const attn_score_params_t *sp, void *stream) {
+  attn::DecodeParams p{};
+  int rc = decode_prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, dt, N, Hq, Hkv, D,
+                          page_size, max_pages_per_seq, num_pages, scale, mk, mp, sk, sp, &p);
+  if (rc) return rc == 1 ? ATTN_OK : rc;
+  // Only the splits this launch takes need room (the workspace of
+  // attn_paged_decode is sized for the smallest split size instead).
+  const int splits = attn::decode_launch_splits(p);
+  const size_t need = decode_partials_bytes(N, Hq, D, splits);
+  if (need > kScratchBytes)
+    return fail(ATTN_ERR_WORKSPACE,
+                "attn_paged_decode_noalloc: %d sequences x %d heads x %d splits need %zu bytes of "
+                "scratch, more than its fixed %zu",
+                N, Hq, splits, need, kScratchBytes);
+  void *base = nullptr;
+  rc = scratch_address((hipStream_t)stream, &base);
+  if (rc) return rc;
+  decode_set_workspace(&p, base, splits);
+  return launch_result(attn::launch_paged_decode(p, (hipStream_t)stream), "attn_paged_decode_noalloc");
 }
 
 int attn_block_mask_transpose(const attn_block_mask_t *bm, int32_t *q_num_blocks, int32_t *q_indices,

@@ -422,6 +422,13 @@ int choose_split_pages(int n_seq, int Hkv, int bound) {
 }
 }  // namespace
 
+int decode_launch_splits(const DecodeParams &p) {
+  const int window = (p.mask.kind == ATTN_MASK_SLIDING) ? p.mask.window : 0;
+  const int bound = pages_bound(p.max_pages, window);
+  const int sp = choose_split_pages(p.N, p.Hkv, bound);
+  return (bound + sp - 1) / sp;
+}
+
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
   DecArgs a;
   a.n_seq = p.N;

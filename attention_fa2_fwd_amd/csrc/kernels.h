@@ -79,6 +79,9 @@ struct DecodeParams {
 // Splits per (sequence, head) the workspace must hold: enough for the
 // smallest split size the launch may choose.
 int decode_max_splits(int max_pages);
+// Splits per (sequence, head) the launch for p takes: the workspace needs
+// room for this many at least (p's workspace fields are not read).
+int decode_launch_splits(const DecodeParams &p);
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);
 
 }  // namespace attn

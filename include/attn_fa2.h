@@ -18,7 +18,9 @@
  *    allocates, frees or keeps a pointer after it returns, and never
  *    synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
  *    default stream) and the caller keeps the buffers alive until the stream
- *    has reached it.
+ *    has reached it.  The one piece of device memory it owns is the fixed
+ *    per-GPU scratch of attn_paged_decode_noalloc, part of the loaded code
+ *    object.
  *  - Return value: 0 on success, negative on failure:
  *      ATTN_ERR_INVALID     (-1) a null pointer, a negative or inconsistent size;
  *      ATTN_ERR_UNSUPPORTED (-2) a valid request outside the supported set;
@@ -259,6 +261,32 @@ int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
                       const attn_mask_params_t *mp, attn_score_kind_t sk,
                       const attn_score_params_t *sp, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* attn_paged_decode_noalloc — attn_paged_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments, meaning,
+ * checks, kernels and results, minus the workspace.  The split partials go
+ * to a scratch array the library holds on each GPU for the life of the
+ * process (64 MiB = 67,108,864 bytes); the first
+ * call on a device looks its address up, with the stream's device current.
+ * The call itself allocates nothing.
+ *   Scratch needed: N * Hq * splits * (D + 1) * 4 bytes (plus padding),
+ *   with splits = the key splits per sequence this launch takes (64 pages
+ *   each, or 32 / 16 when that leaves too few work items), bounded by
+ *   max_pages_per_seq and the window.  A request needing more returns -4
+ *   (ATTN_ERR_WORKSPACE) with the sizes in attn_last_error(); the 64-sequence,
+ *   32-head, 2048-page shape needs 33.8 MB.
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *   on one GPU (different streams, or different host threads without
+ *   ordering) race and may return wrong results; serialise them.  Nothing
+ *   in the scratch has to start at zero (each call writes every partial it
+ *   reads).  The stream must belong to the current device (else -1).        */
+int attn_paged_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *page_table, const int32_t *seq_lens, void *out,
+                              float *lse, attn_dtype_t dt, int N, int Hq, int Hkv, int D,
+                              int page_size, int max_pages_per_seq, int num_pages, float scale,
+                              attn_mask_kind_t mk, const attn_mask_params_t *mp,
+                              attn_score_kind_t sk, const attn_score_params_t *sp, void *stream);
 
 /* Message of the last failed call on this thread ("" if none); valid until
  * the next call on the thread. */

@@ -185,6 +185,28 @@ def test_block_mask_transpose_checks():
     assert lib.attn_block_mask_transpose(ctypes.byref(empty), None, None, None, None) == 0
 
 
+def test_paged_decode_noalloc_rejects_more_than_its_scratch():
+    # Non-null stand-in pointers: the size check refuses the request on the
+    # host before any HIP call, so nothing is dereferenced.  1024 sequences x
+    # 32 heads x 32 splits of 64 pages need 541 MB of partials (> 64 MiB).
+    lib = af.load_library()
+    mp = af.MaskParams(0, 0, None, 0)
+    sp = af.ScoreParams(None, 1.0, 0.0)
+    fake = 256
+    rc = lib.attn_paged_decode_noalloc(fake, fake, fake, fake, fake, fake, fake, 1, 1024, 32, 8, 128,
+                                       16, 2048, 1, 0.1, 0, ctypes.byref(mp), 0, ctypes.byref(sp), None)
+    assert rc == -4
+    msg = lib.attn_last_error().decode()
+    assert "scratch" in msg and "67108864" in msg
+    # the same validation as attn_paged_decode before that
+    assert lib.attn_paged_decode_noalloc(None, None, None, None, None, None, None, 1, 2, 8, 2, 128, 16,
+                                         4, 1, 0.1, 0, ctypes.byref(mp), 0, ctypes.byref(sp), None) == -1
+    assert lib.attn_paged_decode_noalloc(fake, fake, fake, fake, fake, fake, fake, 1, 2, 8, 2, 64, 16,
+                                         4, 1, 0.1, 0, ctypes.byref(mp), 0, ctypes.byref(sp), None) == -2
+    assert lib.attn_paged_decode_noalloc(None, None, None, None, None, None, None, 1, 0, 8, 2, 128, 16,
+                                         4, 1, 0.1, 0, ctypes.byref(mp), 0, ctypes.byref(sp), None) == 0
+
+
 # ---- the binding refuses tensors that do not match the sizes it passes to C
 # (CPU tensors: every shape check runs before the device check, so a refusal
 # here names the shape, and a consistent call gets as far as the device check)
@@ -245,7 +267,7 @@ def _dec_inputs(N=3, Hq=8, Hkv=2, D=128, pages=10, max_pages=4):
             torch.zeros(N, max_pages, dtype=torch.int32), torch.zeros(N, dtype=torch.int32))
 
 
-@pytest.mark.parametrize("fn", ["attn_paged_decode"])
+@pytest.mark.parametrize("fn", ["attn_paged_decode", "attn_paged_decode_noalloc"])
 @pytest.mark.parametrize("change,what", [
     (dict(page_table=torch.zeros(2, 4, dtype=torch.int32)), "page_table"),
     (dict(seq_lens=torch.zeros(4, dtype=torch.int32)), "seq_lens"),

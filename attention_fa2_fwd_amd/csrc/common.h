@@ -150,6 +150,29 @@ __device__ inline int work_ordered_tile(const int32_t *cnt, int n, int cap, int 
   return tile;
 }
 
+// Minimum / maximum of an int over the 64 lanes of a wave, in every lane, by
+// DPP (no LDS traffic): shifts by 1, 2, 4, 8 within each 16-lane row leave
+// the row's result in its lane 15; row_bcast:15 and row_bcast:31 carry it on
+// to rows 1, 3 and then 2, 3, so lane 63 ends with the whole wave's result.
+// Lanes a shift reads nothing for keep their own value (old = src).
+template <bool MIN, int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_step(int v) {
+  const int t = __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+  return MIN ? min(v, t) : max(v, t);
+}
+template <bool MIN>
+__device__ __forceinline__ int wave_reduce_i32(int v) {
+  v = dpp_step<MIN, 0x111, 0xf>(v);   // row_shr:1
+  v = dpp_step<MIN, 0x112, 0xf>(v);   // row_shr:2
+  v = dpp_step<MIN, 0x114, 0xf>(v);   // row_shr:4
+  v = dpp_step<MIN, 0x118, 0xf>(v);   // row_shr:8
+  v = dpp_step<MIN, 0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_step<MIN, 0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_min_i32(int v) { return wave_reduce_i32<true>(v); }
+__device__ __forceinline__ int wave_max_i32(int v) { return wave_reduce_i32<false>(v); }
+
 // Round-to-nearest-even fp32 -> bf16 of two values, packed (lo = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 r = {(__bf16)a, (__bf16)b};

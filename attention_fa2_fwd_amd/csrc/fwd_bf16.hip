@@ -116,15 +116,24 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char *p) {
 //            and one exp2;
 //  kModBias  x = c s + bias, materialised before the max (any bias, or a
 //            scale <= 0);
-//  kModCap   x = C tanh(c s / C), the soft cap, materialised before the max.
-constexpr int kModRaw = 0, kModBias = 1, kModCap = 2;
+//  kModCap   x = C tanh(c s / C), the soft cap, materialised before the max;
+//  kModLin   x = c s + a (j - i), a bias linear in the key-query distance
+//            (ALiBi, relative position) with c > 0, never materialised: the
+//            part a * (offset of the element within its 32-key block) / c is
+//            the C input of the first S MFMA of every block (a constant
+//            register block), so the accumulator holds s + that, and the
+//            per-lane remainder a (block's first key - i) joins the exp2's
+//            addend and the max as one value per block.  The ALiBi path then
+//            costs the raw path's VALU work per score.
+constexpr int kModRaw = 0, kModBias = 1, kModCap = 2, kModLin = 3;
 
 // Compile-time variants: D, the mask kind, the score form MOD and the output
 // dtype.
 template <int D, int MASK, int MOD, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   using C = FwdCfg<D>;
-  constexpr bool GEN = MOD != kModRaw;   // x materialised before the max
+  constexpr bool GEN = MOD == kModBias || MOD == kModCap;   // x materialised before the max
+  constexpr bool LIN = MOD == kModLin;
   // Mask terms: document ids compared (DOCUMENT, and DOCUMENT with a window)
   // and a window on i - j (SLIDING, and DOCUMENT with a window).
   constexpr bool DOC = MASK == ATTN_MASK_DOCUMENT || MASK == kMaskDocWindow;
@@ -138,6 +147,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   __shared__ __align__(16) char v_lds0[C::VTILE];
   __shared__ __align__(16) char v_lds1[C::VTILE];
   __shared__ __align__(16) int32_t kdoc[3][kBN];   // document ids of staged key tiles
+  __shared__ int32_t kdoc_mm[3][2];                // their min and max
   __shared__ __align__(16) int32_t s_blk[kListCap];
   __shared__ uint8_t s_full[kListCap];
 
@@ -178,16 +188,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   const size_t kv_base = ((size_t)(b * a.Hkv + hkv) * a.Skv) * D;
 
   // Q^T fragments: lane holds Q[qi][16c + 8h .. 16c + 8h + 7] (rows past Sq
-  // read row Sq-1 and are never stored).  The empty asm statements make the
-  // loads complete here, so the tile loop never waits on them.
+  // read row Sq-1 and are never stored).  Loaded in the prologue, after the
+  // first tile loads are issued, so the two latencies overlap.
   bf16x8 qf[C::NDC];
-  {
-    const bf16x8 *src = (const bf16x8 *)(a.q + q_base + (size_t)min(qi, a.Sq - 1) * D);
-#pragma unroll
-    for (int c = 0; c < C::NDC; ++c) qf[c] = src[2 * c + h];
-#pragma unroll
-    for (int c = 0; c < C::NDC; ++c) asm volatile("" ::"v"(qf[c]));
-  }
+  const bf16x8 *q_src = (const bf16x8 *)(a.q + q_base + (size_t)min(qi, a.Sq - 1) * D);
 
   // ---- key tiles to visit.  A BlockMask row is staged in LDS so the tile
   // loop reads it without vector memory waits (the host limits a row to
@@ -307,51 +311,87 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   for (int i = 0; i < C::NDB; ++i) o[i] = f32x16{};
 
   const float c_log2 = a.scale_log2;
-  const float bias2 = (MOD == kModBias) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
+  const float bias2 = (MOD == kModBias || LIN) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
+  // kModLin: C input of each 32-key block's first S MFMA, element r being key
+  // 8 (r / 4) + r % 4 of the block (past the lane's 4h), scaled by 1 / c.
+  f32x16 c_lin;
+  if constexpr (LIN) {
+    const float bc = bias2 / c_log2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c_lin[r] = bc * (float)(8 * (r >> 2) + (r & 3));
+  }
   // Soft cap in log2 units and its exponent factor (2 / cap) * c.
   const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
   const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
   const int doc_i = DOC ? doc_row[min(qi, a.Sq - 1)] : 0;
   asm volatile("" ::"v"(doc_i));   // complete the load before the tile loop
+  // Range of the wave's row ids (rows past Sq repeat row Sq - 1): a key tile
+  // whose id range misses it holds no visible key for the wave, and one
+  // whose ids and the rows' are all one id is visible wherever causality
+  // allows.  Neither test assumes sorted ids.
+  const int dmin_w = DOC ? wave_min_i32(doc_i) : 0;
+  const int dmax_w = DOC ? wave_max_i32(doc_i) : 0;
+  // Wave 0 stages a tile's ids (one per lane) with their min and max.
+  auto store_doc = [&](int slot, int id) __attribute__((always_inline)) {
+    kdoc[slot][lane] = id;
+    const int mn = wave_min_i32(id), mx = wave_max_i32(id);
+    if (lane == 0) {
+      kdoc_mm[slot][0] = mn;
+      kdoc_mm[slot][1] = mx;
+    }
+  };
 
-  // Visibility class of a key tile for this wave.
-  auto tile_empty = [&](int k0) __attribute__((always_inline)) -> bool {
+  // Visibility class of a key tile for this wave (dslot: the tile's slot of
+  // staged document ids).
+  auto tile_empty = [&](int k0, int dslot) __attribute__((always_inline)) -> bool {
     bool e = (qw0 >= a.Sq) || (k0 >= a.Skv);
     if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) e = e || (k0 > qw1);
     if (WIN) e = e || (k0 > qw1) || (qw0 - (k0 + kBN - 1) >= a.mask.window);
     if (MASK == ATTN_MASK_PREFIX_LM) e = e || ((k0 > qw1) && (k0 >= a.mask.prefix_len));
+    if (DOC) e = e || (kdoc_mm[dslot][1] < dmin_w) || (kdoc_mm[dslot][0] > dmax_w);
     return e;
   };
-  auto tile_full = [&](int k0, int n) __attribute__((always_inline)) -> bool {
+  auto doc_one_id = [&](int dslot) __attribute__((always_inline)) -> bool {
+    return kdoc_mm[dslot][0] == kdoc_mm[dslot][1] && dmin_w == dmax_w && kdoc_mm[dslot][0] == dmin_w;
+  };
+  auto tile_full = [&](int k0, int n, int dslot) __attribute__((always_inline)) -> bool {
     bool f = (k0 + kBN <= a.Skv);
     if (MASK == ATTN_MASK_CAUSAL) f = f && (k0 + kBN - 1 <= qw0);
-    if (MASK == ATTN_MASK_DOCUMENT) f = f && (k0 + kBN - 1 <= qw0) && tile_block_full(n);
+    if (MASK == ATTN_MASK_DOCUMENT)
+      f = f && (k0 + kBN - 1 <= qw0) && (tile_block_full(n) || doc_one_id(dslot));
     if (MASK == ATTN_MASK_SLIDING) f = f && (k0 + kBN - 1 <= qw0) && (qw1 - k0 < a.mask.window);
     if (MASK == kMaskDocWindow)
-      f = f && (k0 + kBN - 1 <= qw0) && (qw1 - k0 < a.mask.window) && tile_block_full(n);
+      f = f && (k0 + kBN - 1 <= qw0) && (qw1 - k0 < a.mask.window) &&
+          (tile_block_full(n) || doc_one_id(dslot));
     if (MASK == ATTN_MASK_PREFIX_LM) f = f && ((k0 + kBN - 1 <= qw0) || (k0 + kBN <= a.mask.prefix_len));
     return f;
   };
 
+  // Initial accumulator of an S block: zero, or the kModLin bias part.
+  auto s_init = [&]() __attribute__((always_inline)) -> f32x16 {
+    if constexpr (LIN) return c_lin;
+    else return f32x16{};
+  };
   // S^T = K Q^T for the two 32-key blocks of the K tile at kt.
   auto compute_s = [&](f32x16 (&s)[2], const char *kt) __attribute__((always_inline)) {
     const char *kbase = kt + k_rd;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
 #pragma unroll
       for (int c = 0; c < C::NDC; ++c) {
         const bf16x8 ka = *(const bf16x8 *)(kbase + (32 * kb / C::NB) * C::ROWB + 32 * c);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], c > 0 ? s[kb] : s_init(), 0, 0, 0);
       }
     }
   };
 
   // Head of the softmax of one tile (scores s, first key k0, index n): bias,
-  // mask, tile max, threshold rescale of O and l.  Returns the exponent
-  // reference mu.
-  auto softmax_head = [&](f32x16 (&s)[2], int k0, int n, int dslot) __attribute__((always_inline)) -> float {
-    const bool full = tile_full(k0, n);
+  // mask, tile max, threshold rescale of O and l.  Returns the exp2 addend of
+  // each 32-key block: p = 2^(x - mu) is 2^(s + add) on the materialised
+  // forms and 2^(c s + add) on the others (add = -mu, and for kModLin the
+  // block's bias remainder too).
+  auto softmax_head = [&](f32x16 (&s)[2], int k0, int n, int dslot) __attribute__((always_inline)) -> f32x2 {
+    const bool full = tile_full(k0, n, dslot);
     // Accumulator element r of block kb is key j = jb + kb*32 + 8(r/4) + r%4
     // with jb = k0 + 4h.
     const int jb = k0 + 4 * h;
@@ -401,15 +441,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     }
 
     // Tile row max (raw or modified scores), shared by the two halves.  Four
-    // independent partial maxima keep the dependency chain short.
+    // independent partial maxima keep the dependency chain short; two per
+    // 32-key block (kModLin adds each block's bias remainder after the max).
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
-        mx[(r >> 1) & 3] = __builtin_fmaxf(mx[(r >> 1) & 3], __builtin_fmaxf(s[kb][r], s[kb][r + 1]));
-    float tmax = __builtin_fmaxf(__builtin_fmaxf(mx[0], mx[1]), __builtin_fmaxf(mx[2], mx[3]));
-    if constexpr (!GEN) tmax *= c_log2;
+        mx[2 * kb + ((r >> 1) & 1)] =
+            __builtin_fmaxf(mx[2 * kb + ((r >> 1) & 1)], __builtin_fmaxf(s[kb][r], s[kb][r + 1]));
+    // kModLin: the bias of element r of block kb is bias2 (jb + 32 kb - qi)
+    // plus the part already in the accumulator.
+    const float lin0 = LIN ? bias2 * (float)(jb - qi) : 0.0f;
+    const float lin1 = LIN ? __builtin_fmaf(bias2, 32.0f, lin0) : 0.0f;
+    float tmax;
+    if constexpr (LIN) {
+      tmax = __builtin_fmaxf(__builtin_fmaf(__builtin_fmaxf(mx[0], mx[1]), c_log2, lin0),
+                             __builtin_fmaf(__builtin_fmaxf(mx[2], mx[3]), c_log2, lin1));
+    } else {
+      tmax = __builtin_fmaxf(__builtin_fmaxf(mx[0], mx[1]), __builtin_fmaxf(mx[2], mx[3]));
+      if constexpr (!GEN) tmax *= c_log2;
+    }
     tmax = half_swap_max(tmax);
 
     // Raise the reference max only past the threshold (wave-uniform branch).
@@ -422,7 +474,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
 #pragma unroll
       for (int i = 0; i < C::NDB; ++i) o[i] *= alpha;
     }
-    return (m_run == -INFINITY) ? 0.0f : m_run;
+    const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
+    return f32x2{lin0 - mu, lin1 - mu};
   };
 
   // Tail of the softmax: P = 2^(x - mu) and O^T += V^T P^T (V in buffer
@@ -430,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // exp2s.  With WITH_S the S MFMAs of the next tile (K tile kt) are
   // spread over the chunks: one straight-line region in which the matrix
   // cores and the VALU work side by side.
-  auto softmax_tail = [&](auto with_s, f32x16 (&s)[2], float mu, const char *vt, f32x16 (&sn)[2],
+  auto softmax_tail = [&](auto with_s, f32x16 (&s)[2], f32x2 add, const char *vt, f32x16 (&sn)[2],
                           const char *kt) __attribute__((always_inline)) {
     constexpr bool WITH_S = decltype(with_s)::value;
     constexpr int S_PER_CHUNK = 2 * C::NDC / 4;       // S MFMAs per 16-key chunk
@@ -448,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
           const int i = c * S_PER_CHUNK + t;
           const int kb = i / C::NDC, cc = i % C::NDC;
           const bf16x8 ka = *(const bf16x8 *)(kbase + (32 * kb / C::NB) * C::ROWB + 32 * cc);
-          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[cc], cc == 0 ? f32x16{} : sn[kb],
+          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[cc], cc == 0 ? s_init() : sn[kb],
                                                            0, 0, 0);
         }
       }
@@ -459,11 +512,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
       for (int e = 0; e < 8; e += 2) {
         float p0, p1;
         if constexpr (GEN) {
-          p0 = fast_exp2(s[kb][r0 + e] - mu);
-          p1 = fast_exp2(s[kb][r0 + e + 1] - mu);
+          p0 = fast_exp2(s[kb][r0 + e] + add[kb]);
+          p1 = fast_exp2(s[kb][r0 + e + 1] + add[kb]);
         } else {
-          p0 = fast_exp2(__builtin_fmaf(s[kb][r0 + e], c_log2, -mu));
-          p1 = fast_exp2(__builtin_fmaf(s[kb][r0 + e + 1], c_log2, -mu));
+          p0 = fast_exp2(__builtin_fmaf(s[kb][r0 + e], c_log2, add[kb]));
+          p1 = fast_exp2(__builtin_fmaf(s[kb][r0 + e + 1], c_log2, add[kb]));
         }
         // At D=64, where the VALU is the limit, the first chunk seeds the
         // partial sums (0 + x is not folded away: it could change the sign
@@ -495,13 +548,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     load_v(v_lds0, tile_key0(0));
     if (n_tiles > 1) load_k(k_lds1, tile_key0(1));
     if (DOC && wave == 0) {
-      kdoc[0][lane] = load_doc(tile_key0(0));
-      if (n_tiles > 1) kdoc[1][lane] = load_doc(tile_key0(1));
+      store_doc(0, load_doc(tile_key0(0)));
+      if (n_tiles > 1) store_doc(1, load_doc(tile_key0(1)));
     }
-    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0)
   }
+  // The empty asm statements make the Q loads complete here, so the tile
+  // loop never waits on them.
+#pragma unroll
+  for (int c = 0; c < C::NDC; ++c) qf[c] = q_src[2 * c + h];
+#pragma unroll
+  for (int c = 0; c < C::NDC; ++c) asm volatile("" ::"v"(qf[c]));
+  if (n_tiles > 0) __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0)
   __syncthreads();
-  if (n_tiles > 0 && !tile_empty(tile_key0(0))) compute_s(sa, k_lds0);
+  if (n_tiles > 0 && !tile_empty(tile_key0(0), 0)) compute_s(sa, k_lds0);
   // Iteration 0 refills K buffer 0 (tile 2): every wave must be done reading
   // tile 0 from it first.  Later refills target a buffer last read before
   // the previous iteration's barrier.
@@ -527,25 +586,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     }
     if (n + 1 < n_tiles) load_v(v_fill, tile_key0(n + 1));
     __builtin_amdgcn_s_setprio(0);
-    const bool cur_live = !tile_empty(k0);
-    const bool next_live = (n + 1 < n_tiles) && !tile_empty(tile_key0(n + 1));
+    const bool cur_live = !tile_empty(k0, n % 3);
+    const bool next_live = (n + 1 < n_tiles) && !tile_empty(tile_key0(n + 1), (n + 1) % 3);
     if (cur_live) {
       // The next tile's S is computed whether or not that tile is live for
       // this wave (a dead or absent tile reads a stale, valid K buffer and
       // the result is never used): one code path keeps the whole tail in a
       // single scheduling region.
-      const float mu = softmax_head(s_cur, k0, n, n % 3);
+      const f32x2 add = softmax_head(s_cur, k0, n, n % 3);
       // The tail (exp2, P·V and the next tile's S on the matrix cores) runs
       // at raised wave priority, so a wave there issues ahead of waves in
       // their softmax head or waiting on loads: measured 6-7% faster on
       // causal and 4-5% on the GQA window workload, dense unchanged.
       __builtin_amdgcn_s_setprio(1);
-      softmax_tail(std::true_type{}, s_cur, mu, v_cur, s_next, k_next);
+      softmax_tail(std::true_type{}, s_cur, add, v_cur, s_next, k_next);
       __builtin_amdgcn_s_setprio(0);
     } else if (next_live) {
       compute_s(s_next, k_next);
     }
-    if (DOC && wave == 0 && n + 2 < n_tiles) kdoc[(n + 2) % 3][lane] = doc_fill;
+    if (DOC && wave == 0 && n + 2 < n_tiles) store_doc((n + 2) % 3, doc_fill);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads and LDS stores are done
     __syncthreads();
   };
@@ -637,10 +696,14 @@ hipError_t launch_d(const FwdParams &p, hipStream_t stream) {
     return p.out_f32 ? launch_mask<D, kModCap, true>(a, p.mask.kind, grid, stream)
                      : launch_mask<D, kModCap, false>(a, p.mask.kind, grid, stream);
   }
-  // The raw-score path needs a positive scale and no bias.
-  if (p.score.kind != ATTN_SCORE_NONE || !(a.scale_log2 > 0.0f)) {
+  // The raw-score and linear-bias paths need a positive scale.
+  if (!(a.scale_log2 > 0.0f)) {
     return p.out_f32 ? launch_mask<D, kModBias, true>(a, p.mask.kind, grid, stream)
                      : launch_mask<D, kModBias, false>(a, p.mask.kind, grid, stream);
+  }
+  if (p.score.kind != ATTN_SCORE_NONE) {   // ALIBI, REL_POS: a (j - i)
+    return p.out_f32 ? launch_mask<D, kModLin, true>(a, p.mask.kind, grid, stream)
+                     : launch_mask<D, kModLin, false>(a, p.mask.kind, grid, stream);
   }
   return p.out_f32 ? launch_mask<D, kModRaw, true>(a, p.mask.kind, grid, stream)
                    : launch_mask<D, kModRaw, false>(a, p.mask.kind, grid, stream);

@@ -383,17 +383,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       load_tile(v_nxt, v_rsrc, k1);
       if (DOC && wave == 0) doc_fill = load_doc(k1);
     }
-    tile_step(k0, tile_flag(n), k_cur, v_cur, d_cur);
+    if (n < n_tiles) tile_step(k0, tile_flag(n), k_cur, v_cur, d_cur);
     if (DOC && wave == 0 && n + 1 < n_tiles) d_nxt[lane] = doc_fill;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  int n = 0;
-  for (; n + 1 < n_tiles; n += 2) {
+  // Tiles in pairs; an odd count ends with an empty visit (its barrier
+  // only), so the tile body is built twice rather than three times.
+  for (int n = 0; n < n_tiles; n += 2) {
     iteration(n, k_lds0, v_lds0, kdoc0, k_lds1, v_lds1, kdoc1);
     iteration(n + 1, k_lds1, v_lds1, kdoc1, k_lds0, v_lds0, kdoc0);
   }
-  if (n < n_tiles) iteration(n, k_lds0, v_lds0, kdoc0, k_lds1, v_lds1, kdoc1);
 
   // dQ = s dX K: lane holds dQ^T[32 db + 8 g + 4h + e][qi].
   if (qi < a.Sq) {
@@ -625,8 +625,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       const int qo = 8 * g + 4 * h;   // query offset of elements 4g .. 4g + 3
       const f32x4 l4 = *(const f32x4 *)(ls + qo);
       const f32x4 d4 = *(const f32x4 *)(dt + qo);
+      // Document masks read the group's ids on every tile and select
+      // without a branch: a branch on `full` here doubles the live set of
+      // the D = 128 variants and sends K to scratch.
       int4 c4 = int4{0, 0, 0, 0};
-      if (DOC && !full) c4 = *(const int4 *)(dc + qo);
+      if (DOC) c4 = *(const int4 *)(dc + qo);
       float pr[4], dr[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -634,9 +637,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
         const int i = i0 + qo + e;
         const float x = mod_score<MOD>(s[r], c_log2, bias2, cap_k, cap2, bias_base, (float)(-(8 * g + e)));
         float pe = fast_exp2(x - l4[e]);
-        if (!full) {
+        if (DOC) {
           const int doc_i = (e == 0) ? c4.x : (e == 1) ? c4.y : (e == 2) ? c4.z : c4.w;
-          pe = pair_visible<MASK>(a.mask, i, kj, doc_i, doc_j) ? pe : 0.0f;
+          pe = (full || pair_visible<MASK>(a.mask, i, kj, doc_i, doc_j)) ? pe : 0.0f;
+        } else if (!full) {
+          pe = pair_visible<MASK>(a.mask, i, kj, 0, 0) ? pe : 0.0f;
         }
         pr[e] = pe;
         dr[e] = pe * (dp[r] - d4[e]) * mod_grad<MOD>(x, inv_cap2);
@@ -688,22 +693,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       load_tiles(nx, q_nxt, o_nxt);
       if (wave == 0) nv = fetch_qvals(nx);
     }
-    tile_step(st, q_cur, o_cur, l_cur, d_cur, c_cur);
+    if (it < n_iter) tile_step(st, q_cur, o_cur, l_cur, d_cur, c_cur);
     if (wave == 0 && it + 1 < n_iter) store_qvals(nv, l_nxt, d_nxt, c_nxt);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
+  // Steps in pairs; an odd count ends with an empty step (its barrier only),
+  // so the step body is built twice, not three times: a third copy pushed
+  // the D = 128 document variants over the register budget.
   int it = 0;
   Step st = first;
-  for (; it + 1 < n_iter; it += 2) {
+  for (; it < n_iter; it += 2) {
     iteration(it, st, q_lds0, o_lds0, qv_lse0, qv_dot0, qv_doc0, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1);
     st = next_step(st);
     iteration(it + 1, st, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1, q_lds0, o_lds0, qv_lse0, qv_dot0,
               qv_doc0);
     st = next_step(st);
   }
-  if (it < n_iter)
-    iteration(it, st, q_lds0, o_lds0, qv_lse0, qv_dot0, qv_doc0, q_lds1, o_lds1, qv_lse1, qv_dot1, qv_doc1);
 
   // dK = s dX^T Q, dV = P^T dO: lane holds X^T[32 db + 8 g + 4h + e][kj].
   if (kj < a.Skv) {

@@ -160,7 +160,13 @@ int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
              const attn_block_mask_t *bm, void *stream);
 
 /* attn_build_block_mask — BlockMask of mask kind `mk` (same predicate as
- * attn_fwd) for B x Sq x Skv, in q_block x kv_block blocks.
+ * attn_fwd) for B x Sq x Skv, in q_block x kv_block blocks.  The FlexAttention
+ * write-up's introduction says the kernel exploits the sparsity of the mask
+ * by skipping fully masked blocks; this call computes that block structure
+ * once, for reuse by every attn_fwd / attn_bwd call with the same mask (the
+ * write-up gives no layout: the one below, per query block an ascending list
+ * of the key blocks that hold a visible pair plus a flag for blocks where
+ * every pair is visible, is this library's).
  *   kv_num_blocks int32 [B, 1, ceil(Sq/q_block)]                 (written)
  *   kv_indices    int32 [B, 1, ceil(Sq/q_block), ceil(Skv/kv_block)] (written)
  *   kv_full       uint8 same shape as kv_indices, or NULL         (written)
@@ -184,8 +190,9 @@ int attn_build_block_mask(attn_mask_kind_t mk, const attn_mask_params_t *mp, int
 int attn_block_mask_transpose(const attn_block_mask_t *bm, int32_t *q_num_blocks, int32_t *q_indices,
                               uint8_t *q_full, void *stream);
 
-/* attn_bwd_workspace_size — bytes of device scratch attn_bwd needs: one
- * float per query row, B * Hq * Sq * 4, rounded up to 256.                  */
+/* attn_bwd_workspace_size — bytes of device scratch attn_bwd needs (the
+ * pages say nothing of it; this library's choice): one float per query row,
+ * the row term D = rowsum(dO * O), B * Hq * Sq * 4, rounded up to 256.     */
 size_t attn_bwd_workspace_size(int B, int Hq, int Sq);
 
 /* attn_bwd — gradients of attn_fwd from its stored LSE.  The FlexAttention
@@ -220,8 +227,9 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
              void *workspace, size_t workspace_bytes, void *stream);
 
 /* attn_paged_decode_workspace_size — bytes of device scratch attn_paged_decode
- * needs for this shape: fp32 partial outputs and log-sum-exps of every key
- * split, for splits as small as 16 pages (the launch takes 64-page splits,
+ * needs for this shape (the pages say nothing of a split-KV workspace; its
+ * size and layout are this library's): fp32 partial outputs and
+ * log-sum-exps of every key split, for splits as small as 16 pages (the launch takes 64-page splits,
  * or 32 / 16 when that leaves too few work items), sized from
  * max_pages_per_seq so the host never reads seq_lens:
  * N * Hq * ceil(max_pages_per_seq / 16) * (D + 1) * 4 bytes, plus padding. */

@@ -410,9 +410,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = softcap_log2_fast(s[kb][r], cap_k, cap2);
     }
-    if (!full) {
-      // Partial tile: the mask predicate per element; -inf where hidden (for
-      // the raw scores too: c > 0 on that path).
+    if (!full && !DOC) {
+      // Partial tile, masks of positions only: every kind's visible keys of
+      // a row form one interval of offsets, lo <= off <= hi (CAUSAL and
+      // SLIDING end at the diagonal, PREFIX_LM at the later of the diagonal
+      // and the prefix end, and all at the last key; SLIDING starts W - 1
+      // keys before the diagonal), tested as one unsigned compare per
+      // element: (hi - off) < (hi - lo + 1).  -inf where hidden (for the
+      // raw scores too: c > 0 on that path).
+      const int dq = qi - jb;                       // j <= qi  <=>  off <= dq
+      int hi = a.Skv - jb - 1;
+      int lo = 0;
+      if (MASK == ATTN_MASK_CAUSAL || WIN) hi = min(hi, dq);
+      if (MASK == ATTN_MASK_PREFIX_LM) hi = min(hi, max(dq, a.mask.prefix_len - jb - 1));
+      if (WIN) lo = dq - a.mask.window + 1;
+      const unsigned span = (hi >= lo) ? (unsigned)(hi - lo) + 1u : 0u;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = ((unsigned)(hi - off) < span) ? s[kb][r] : -INFINITY;
+        }
+    }
+    if (!full && DOC) {
+      // Partial tile under a document mask: the predicate per element,
+      // with the key ids staged in LDS.
       const int dq = qi - jb;                       // j <= qi  <=>  off <= dq
       int32_t kd[2][4][4];
       if (DOC) {

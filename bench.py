@@ -6,7 +6,9 @@ single-GPU prefill configuration: bf16 GQA sliding window 1024 + ALiBi,
 B=2, Hq=32, Hkv=8, S=8192, D=128, seed 0, inputs already resident in HBM.
 The JSON line reports unmasked TFLOP/s (4*D FLOPs per visible (query, key)
 pair) against the 2.5 PFLOP/s dense bf16 MFMA peak, with the forward kernel's
-launch times (mean, median, min) from HIP events on the launch stream; a
+launch times (mean, median, min) from HIP events on the launch stream (after
+0.3 s of back-to-back launches that bring the GPU to its steady clocks, then
+the W counted warm-up steps); a
 second roofline block for the paged decode of 64 sequences (HBM bytes
 against 8 TB/s); the CPU oracle timed on (batch, head) slices of the
 benchmarked tensors; and per-workload figures for the other prefill shapes,
@@ -89,8 +91,27 @@ def time_launches(torch, fn, steps: int):
     return {"mean_ms": evs[0].elapsed_time(evs[steps]) / steps, "median_ms": median, "min_ms": per[0]}
 
 
+PREWARM_S = 0.3   # seconds of back-to-back work before the counted warm-up steps
+
+
+def prewarm(torch, fn, seconds: float = PREWARM_S) -> int:
+    """Run fn back to back for about `seconds` of wall-clock time.  The GPU
+    takes some tens of ms of continuous work to reach its steady clocks
+    (launches of the GQA window workload run ~20% slower over the first
+    ~20 ms); this runs before the W counted warm-up steps so that the K
+    timed steps see the steady state.  Returns the launches run."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            fn()
+        torch.cuda.synchronize()
+        n += 16
+    return n
+
+
 def bench_prefill(af, torch, workloads, w, steps, warmup, out_dtype=None, with_block_mask=None,
-                  inputs=None):
+                  inputs=None, prewarm_s: float = 0.0):
     """attn_fwd on a prefill workload; the BlockMask (when the workload has
     one) is built once, timed on its own and reused by every launch."""
     dev = torch.device("cuda")
@@ -115,6 +136,8 @@ def bench_prefill(af, torch, workloads, w, steps, warmup, out_dtype=None, with_b
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     kw = dict(scale=1.0 / math.sqrt(w.D), mask=w.mask, window=w.window, prefix_len=w.prefix_len,
               doc_ids=doc, score=w.score, softcap=w.softcap, block_mask=bm, out=out, lse=lse)
+    if prewarm_s > 0:
+        prewarm(torch, lambda: af.attn_fwd(q, k, v, **kw), prewarm_s)
     for _ in range(warmup):
         af.attn_fwd(q, k, v, **kw)
     torch.cuda.synchronize()
@@ -130,7 +153,7 @@ def bench_prefill(af, torch, workloads, w, steps, warmup, out_dtype=None, with_b
     return res
 
 
-def bench_backward(af, torch, workloads, w, steps, warmup):
+def bench_backward(af, torch, workloads, w, steps, warmup, prewarm_s: float = 0.0):
     """attn_bwd on a prefill workload (its forward run once for O and LSE).
     Algorithmic FLOPs: 10 D per visible pair (the products S, dP, dV, dK,
     dQ: 2.5 times the forward's), whatever the kernels recompute."""
@@ -154,6 +177,9 @@ def bench_backward(af, torch, workloads, w, steps, warmup):
     dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
     ws = torch.empty(max(int(af.load_library().attn_bwd_workspace_size(w.B, w.Hq, w.Sq)), 1),
                      dtype=torch.uint8, device=dev)
+    if prewarm_s > 0:
+        prewarm(torch, lambda: af.attn_bwd(q, k, v, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw),
+                prewarm_s)
     for _ in range(warmup):
         af.attn_bwd(q, k, v, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
     torch.cuda.synchronize()
@@ -179,7 +205,7 @@ def decode_algorithmic_bytes(w, lengths, window=0, hq=None):
     return kv_bytes + n * hq * w.D * 2 * 2 + n * hq * 4 + pages * 4 + n * 4, tokens
 
 
-def bench_decode(af, torch, workloads, steps, warmup, window=0, score="none"):
+def bench_decode(af, torch, workloads, steps, warmup, window=0, score="none", prewarm_s: float = 0.0):
     """Paged decode of the 64-sequence workload; with window > 0 each query
     sees its last `window` keys (and only those are counted as read)."""
     dev = torch.device("cuda")
@@ -193,6 +219,8 @@ def bench_decode(af, torch, workloads, steps, warmup, window=0, score="none"):
     args = (inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"], inp["seq_lens"])
     kw = dict(scale=1.0 / math.sqrt(d), workspace=ws, out=out, lse=lse,
               mask="sliding" if window else "none", window=window, score=score)
+    if prewarm_s > 0:
+        prewarm(torch, lambda: af.attn_paged_decode(*args, **kw), prewarm_s)
     for _ in range(warmup):
         af.attn_paged_decode(*args, **kw)
     torch.cuda.synchronize()
@@ -322,13 +350,15 @@ def main():
             wl = {"bwd_causal": workloads.CAUSAL_BF16, "bwd_gqa": workloads.GQA_WINDOW_ALIBI,
                   "bwd_dense": workloads.DENSE_BF16,
                   "bwd_document": workloads.DOCUMENT_BLOCKMASK}[args.only]
-            r = bench_backward(af, torch, workloads, wl, args.steps, args.warmup)
+            r = bench_backward(af, torch, workloads, wl, args.steps, args.warmup, prewarm_s=PREWARM_S)
         elif args.only == "decode":
-            r = bench_decode(af, torch, workloads, args.steps, args.warmup)
+            r = bench_decode(af, torch, workloads, args.steps, args.warmup, prewarm_s=PREWARM_S)
         elif args.only == "decode_window":
-            r = bench_decode(af, torch, workloads, args.steps, args.warmup, window=1024, score="alibi")
+            r = bench_decode(af, torch, workloads, args.steps, args.warmup, window=1024, score="alibi",
+                             prewarm_s=PREWARM_S)
         elif args.only in sel:
-            r = bench_prefill(af, torch, workloads, sel[args.only], args.steps, args.warmup)
+            r = bench_prefill(af, torch, workloads, sel[args.only], args.steps, args.warmup,
+                              prewarm_s=PREWARM_S)
         else:
             ap.error(f"--only takes one of: {ONLY}")
         print(json.dumps({"workload": args.only, **r}), flush=True)
@@ -346,10 +376,12 @@ def main():
     def step():
         af.attn_fwd(q, k, v, scale=scale, mask=w.mask, window=w.window, score=w.score, out=out, lse=lse)
 
+    prewarm_launches = prewarm(torch, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] warmup done ({prewarm_launches} pre-warm launches, {args.warmup} steps)",
+          file=sys.stderr, flush=True)
     t = time_launches(torch, step, args.steps)     # synchronised on both sides
     ms_step = t["mean_ms"]
     pairs = visible_pairs(w.mask, w.Sq, w.window)
@@ -385,6 +417,8 @@ def main():
                                    "min": round(t["min_ms"], 5)},
                      "tflops_at_median": round(flops / (t["median_ms"] * 1e-3) / 1e12, 3)},
         "cpu_baseline": None,
+        "prewarm": {"seconds": PREWARM_S, "launches": prewarm_launches,
+                    "why": "the timed steps run at the GPU's steady clocks"},
     }
 
     # ---- paged decode roofline (HBM), 64 sequences

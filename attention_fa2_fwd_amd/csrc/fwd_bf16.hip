@@ -154,6 +154,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;   // kept per-lane: branches on it stay exec-masked, which keeps the schedule tight
+  // The same index in a scalar register, for the tile loads' LDS
+  // destinations (M0 takes a scalar; computed from the per-lane index they
+  // would hold a vector register each).
+  const int wave_s = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;      // lane half: selects keys 4h..4h+3 of each 8
   const int l32 = lane & 31;    // query column of this lane
 
@@ -262,23 +266,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   const __amdgpu_buffer_rsrc_t d_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(doc_row ? doc_row : a.mask.doc_ids), (short)0, doc_row ? a.Skv * 4 : 0, kBufferFlags);
   // Byte offset of this lane's chunk for load i = 0; load i is 4 rows
-  // further on.  key0 is wave-uniform; on the BlockMask path it comes from
-  // LDS, so it is moved to a scalar register explicitly (it is the loads'
-  // scalar offset).
+  // further on, which goes into the scalar offset with the tile's own.  key0
+  // is wave-uniform; on the BlockMask path it comes from LDS, so it is moved
+  // to a scalar register explicitly.
   const int ld_off = ((wave + C::NB * (lane / C::CPR)) * D + (lane % C::CPR) * 8) * 2;
   auto load_k = [&](char *dst, int key0) __attribute__((always_inline)) {
     const int soff = __builtin_amdgcn_readfirstlane(key0 * D * 2);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void *)(dst + (4 * i + wave) * C::KBLK), 16,
-                                               ld_off + i * (4 * D * 2), soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void *)(dst + (4 * i + wave_s) * C::KBLK), 16,
+                                               ld_off, soff + i * (4 * D * 2), 0, 0);
   };
   auto load_v = [&](char *dst, int key0) __attribute__((always_inline)) {
     const int soff = __builtin_amdgcn_readfirstlane(key0 * D * 2);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void *)(dst + (4 * i + wave) * C::VBLK), 16,
-                                               ld_off + i * (4 * D * 2), soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void *)(dst + (4 * i + wave_s) * C::VBLK), 16,
+                                               ld_off, soff + i * (4 * D * 2), 0, 0);
   };
   // Document ids of a key tile go through wave 0's registers into kdoc (a
   // plain LDS store, so later reads of kdoc never wait for the buffer->LDS
@@ -505,26 +509,51 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // tile vt), one 16-key chunk at a time, each chunk's P·V MFMAs right after its
   // exp2s.  With WITH_S the S MFMAs of the next tile (K tile kt) are
   // spread over the chunks: one straight-line region in which the matrix
-  // cores and the VALU work side by side.
+  // cores and the VALU work side by side.  LDS reads are issued ahead of
+  // their use, each chunk's V fragments at its start and the K fragments a
+  // whole chunk early, and scheduling barriers keep the compiler from
+  // sinking them back next to their MFMAs (measured 4-8% faster than reads
+  // placed by the scheduler).
   auto softmax_tail = [&](auto with_s, f32x16 (&s)[2], f32x2 add, const char *vt, f32x16 (&sn)[2],
                           const char *kt) __attribute__((always_inline)) {
     constexpr bool WITH_S = decltype(with_s)::value;
     constexpr int S_PER_CHUNK = 2 * C::NDC / 4;       // S MFMAs per 16-key chunk
     const char *vbase = vt + v_rd;
     const char *kbase = kt + k_rd;
-    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // independent partial row sums
+    float ps[4];   // independent partial row sums, seeded by the first chunk
+    // K fragment i of the next tile's S MFMAs (block i / NDC, d chunk i % NDC).
+    auto k_frag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      const int kb = i / C::NDC, cc = i % C::NDC;
+      return *(const bf16x8 *)(kbase + (32 * kb / C::NB) * C::ROWB + 32 * cc);
+    };
+    bf16x8 kf[2][S_PER_CHUNK];   // this chunk's K fragments and the next chunk's
+    if constexpr (WITH_S) {
+#pragma unroll
+      for (int t = 0; t < S_PER_CHUNK; ++t) kf[0][t] = k_frag(t);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      // Keep each chunk's LDS reads in the chunk: hoisted further they would
-      // only hold registers longer.
-      asm volatile("" ::: "memory");
+      // Reads first: the next chunk's K fragments and this chunk's V^T.
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (WITH_S) {
+        if (c + 1 < 4) {
+#pragma unroll
+          for (int t = 0; t < S_PER_CHUNK; ++t) kf[(c + 1) & 1][t] = k_frag((c + 1) * S_PER_CHUNK + t);
+        }
+      }
+      s16x4 vlo[C::NDB], vhi[C::NDB];
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        vlo[db] = lds_read_tr(vbase + v_key_off(16 * c) + 64 * db);
+        vhi[db] = lds_read_tr(vbase + v_key_off(16 * c + 8) + 64 * db);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (WITH_S) {
 #pragma unroll
         for (int t = 0; t < S_PER_CHUNK; ++t) {
           const int i = c * S_PER_CHUNK + t;
           const int kb = i / C::NDC, cc = i % C::NDC;
-          const bf16x8 ka = *(const bf16x8 *)(kbase + (32 * kb / C::NB) * C::ROWB + 32 * cc);
-          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[cc], cc == 0 ? s_init() : sn[kb],
+          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c & 1][t], qf[cc], cc == 0 ? s_init() : sn[kb],
                                                            0, 0, 0);
         }
       }
@@ -541,18 +570,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
           p0 = fast_exp2(__builtin_fmaf(s[kb][r0 + e], c_log2, add[kb]));
           p1 = fast_exp2(__builtin_fmaf(s[kb][r0 + e + 1], c_log2, add[kb]));
         }
-        // At D=64, where the VALU is the limit, the first chunk seeds the
-        // partial sums (0 + x is not folded away: it could change the sign
-        // of a zero), measured 1-4% faster; at D=128 the changed schedule
-        // measured 1-2% slower, so the sums start from zero there.
-        if (D == 64 && c == 0) ps[e >> 1] = p0 + p1; else ps[e >> 1] += p0 + p1;
+        // The first chunk seeds the partial sums rather than adding to zero
+        // (0 + x is not folded away: it could change the sign of a zero).
+        if (c == 0) ps[e >> 1] = p0 + p1; else ps[e >> 1] += p0 + p1;
         pw[e >> 1] = pack_bf16x2(p0, p1);
       }
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      // The sums are formed here, so the chunk's fp32 p values die with it
+      // instead of staying live until the end of the tile.
+      asm volatile("" : "+v"(ps[0]), "+v"(ps[1]), "+v"(ps[2]), "+v"(ps[3]));
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        const s16x4 lo = lds_read_tr(vbase + v_key_off(16 * c) + 64 * db);
-        const s16x4 hi = lds_read_tr(vbase + v_key_off(16 * c + 8) + 64 * db);
+        const s16x4 lo = vlo[db];
+        const s16x4 hi = vhi[db];
         const u32x4 vw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pb,

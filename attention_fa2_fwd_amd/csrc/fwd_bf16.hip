@@ -62,11 +62,8 @@ namespace attn {
 namespace {
 
 constexpr int kBM = 128;       // query rows per workgroup
-constexpr int kBN = 64;        // key rows per tile
-// Key tiles per BlockMask block: the host accepts only 128-wide key blocks on
-// this path, so a tile's block and part are a shift and a mask.
-constexpr int kTilesPerBlock = 128 / kBN;
-static_assert(kTilesPerBlock == 2, "block = tile index >> 1");
+// BlockMask blocks on this path are 128 keys wide (host-checked).
+constexpr int kMaskBlock = 128;
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kListCap = 1024; // BlockMask entries staged in LDS per query tile (host-checked)
 static_assert(2 * kOrderCap <= kListCap, "work-ordering scratch fits the list buffer");
@@ -75,10 +72,20 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr int kKPad = 16;      // bytes between K row blocks
 constexpr int kVPad = 64;      // bytes between V row blocks
 
-template <int D>
+// D and the key-tile length BN: 128 at D = 64 without a mask, where the
+// per-tile fixed work (loads, max, barrier) would otherwise weigh on only 16
+// MFMAs (measured +6% on dense D = 64; under causal-type masks the longer
+// tiles lose more on the diagonal than they gain, so those keep 64).
+template <int D, int BN_>
 struct FwdCfg {
+  static constexpr int BN = BN_;                  // key rows per tile
+  static constexpr int KB = BN / 32;              // 32-key blocks of S^T per tile
+  static constexpr int NCH = BN / 16;             // 16-key chunks of P per tile
+  static constexpr int TPB = kMaskBlock / BN;     // tiles per BlockMask block
+  static constexpr int TPB_SHIFT = TPB == 2 ? 1 : 0;
+  static_assert(TPB == 1 << TPB_SHIFT, "tile -> block is a shift");
   static constexpr int ROWB = D * 2;              // bytes of one K/V row
-  static constexpr int NB = kBN * ROWB / 1024;    // 1 KiB row blocks per tile (16 or 8)
+  static constexpr int NB = BN * ROWB / 1024;     // 1 KiB row blocks per tile (8 or 16)
   static constexpr int KBLK = 1024 + kKPad;
   static constexpr int VBLK = 1024 + kVPad;
   static constexpr int KTILE = NB * KBLK;         // bytes
@@ -131,13 +138,15 @@ constexpr int kModRaw = 0, kModBias = 1, kModCap = 2, kModLin = 3;
 // dtype.
 template <int D, int MASK, int MOD, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
-  using C = FwdCfg<D>;
   constexpr bool GEN = MOD == kModBias || MOD == kModCap;   // x materialised before the max
   constexpr bool LIN = MOD == kModLin;
   // Mask terms: document ids compared (DOCUMENT, and DOCUMENT with a window)
   // and a window on i - j (SLIDING, and DOCUMENT with a window).
   constexpr bool DOC = MASK == ATTN_MASK_DOCUMENT || MASK == kMaskDocWindow;
   constexpr bool WIN = MASK == ATTN_MASK_SLIDING || MASK == kMaskDocWindow;
+  using C = FwdCfg<D, (D == 64 && MASK == ATTN_MASK_NONE) ? 128 : 64>;
+  constexpr int kBN = C::BN;
+  static_assert(!DOC || kBN == 64, "document ids are staged one per lane");
   // K and V double buffers as four distinct LDS objects, always addressed
   // through their own names: the compiler can then tell that reading one
   // buffer does not depend on buffer->LDS loads still in flight to another,
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   __shared__ __align__(16) char k_lds1[C::KTILE];
   __shared__ __align__(16) char v_lds0[C::VTILE];
   __shared__ __align__(16) char v_lds1[C::VTILE];
-  __shared__ __align__(16) int32_t kdoc[3][kBN];   // document ids of staged key tiles
+  __shared__ __align__(16) int32_t kdoc[3][64];    // document ids of staged key tiles (BN = 64)
   __shared__ int32_t kdoc_mm[3][2];                // their min and max
   __shared__ __align__(16) int32_t s_blk[kListCap];
   __shared__ uint8_t s_full[kListCap];
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     // Counts and indices are device data: clamp them so a malformed list
     // can only drop tiles, never address outside K/V.
     const int n_blocks = min(max(a.bm_num[row], 0), min(a.bm_nkb, kListCap));
-    n_tiles = n_blocks * kTilesPerBlock;
+    n_tiles = n_blocks * C::TPB;
     bm_list = a.bm_idx + row * a.bm_nkb;
     if (a.bm_full) bm_flags = a.bm_full + row * a.bm_nkb;
     for (int t = tid; t < n_blocks; t += kThreads) {
@@ -239,17 +248,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   auto tile_key0 = [&](int n) __attribute__((always_inline)) -> int {
     n = n_tiles - 1 - n;
     if (bm_list) {
-      const int bi = n >> 1;
+      const int bi = n >> C::TPB_SHIFT;   // n >= 0
       const int blk = s_blk[bi];   // bi < n_blocks <= kListCap
       if (blk < 0 || blk >= a.bm_nkb) return a.Skv;      // treated as an empty tile
-      return blk * (kTilesPerBlock * kBN) + (n & 1) * kBN;
+      return blk * kMaskBlock + (n & (C::TPB - 1)) * kBN;
     }
     return (t_first + n) * kBN;
   };
   auto tile_block_full = [&](int n) __attribute__((always_inline)) -> bool {
     n = n_tiles - 1 - n;
     if (!bm_flags) return false;
-    const int bi = n >> 1;
+    const int bi = n >> C::TPB_SHIFT;
     return s_full[bi] != 0;
   };
 
@@ -377,10 +386,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     else return f32x16{};
   };
   // S^T = K Q^T for the two 32-key blocks of the K tile at kt.
-  auto compute_s = [&](f32x16 (&s)[2], const char *kt) __attribute__((always_inline)) {
+  auto compute_s = [&](f32x16 (&s)[C::KB], const char *kt) __attribute__((always_inline)) {
     const char *kbase = kt + k_rd;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
       for (int c = 0; c < C::NDC; ++c) {
         const bf16x8 ka = *(const bf16x8 *)(kbase + (32 * kb / C::NB) * C::ROWB + 32 * c);
@@ -394,7 +403,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // each 32-key block: p = 2^(x - mu) is 2^(s + add) on the materialised
   // forms and 2^(c s + add) on the others (add = -mu, and for kModLin the
   // block's bias remainder too).
-  auto softmax_head = [&](f32x16 (&s)[2], int k0, int n, int dslot) __attribute__((always_inline)) -> f32x2 {
+  auto softmax_head = [&](f32x16 (&s)[C::KB], int k0, int n, int dslot, float (&add)[C::KB])
+                          __attribute__((always_inline)) {
     const bool full = tile_full(k0, n, dslot);
     // Accumulator element r of block kb is key j = jb + kb*32 + 8(r/4) + r%4
     // with jb = k0 + 4h.
@@ -402,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     if constexpr (MOD == kModBias) {
       const float cb = bias2 * (float)(jb - qi);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float off = (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
@@ -410,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
         }
     } else if constexpr (MOD == kModCap) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = softcap_log2_fast(s[kb][r], cap_k, cap2);
     }
@@ -430,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
       if (WIN) lo = dq - a.mask.window + 1;
       const unsigned span = (hi >= lo) ? (unsigned)(hi - lo) + 1u : 0u;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
@@ -441,10 +451,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
       // Partial tile under a document mask: the predicate per element,
       // with the key ids staged in LDS.
       const int dq = qi - jb;                       // j <= qi  <=>  off <= dq
-      int32_t kd[2][4][4];
+      int32_t kd[C::KB][4][4];
       if (DOC) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int4 t = *(const int4 *)&kdoc[dslot][kb * 32 + 8 * g + 4 * h];
@@ -452,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
           }
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
@@ -470,23 +480,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     // Tile row max (raw or modified scores), shared by the two halves.  Four
     // independent partial maxima keep the dependency chain short; two per
     // 32-key block (kModLin adds each block's bias remainder after the max).
-    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float mx[2 * C::KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < 2 * C::KB; ++i) mx[i] = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
         mx[2 * kb + ((r >> 1) & 1)] =
             __builtin_fmaxf(mx[2 * kb + ((r >> 1) & 1)], __builtin_fmaxf(s[kb][r], s[kb][r + 1]));
     // kModLin: the bias of element r of block kb is bias2 (jb + 32 kb - qi)
     // plus the part already in the accumulator.
-    const float lin0 = LIN ? bias2 * (float)(jb - qi) : 0.0f;
-    const float lin1 = LIN ? __builtin_fmaf(bias2, 32.0f, lin0) : 0.0f;
-    float tmax;
+    float lin[C::KB];
+    lin[0] = LIN ? bias2 * (float)(jb - qi) : 0.0f;
+#pragma unroll
+    for (int kb = 1; kb < C::KB; ++kb) lin[kb] = LIN ? __builtin_fmaf(bias2, 32.0f * kb, lin[0]) : 0.0f;
+    float tmax = -INFINITY;
     if constexpr (LIN) {
-      tmax = __builtin_fmaxf(__builtin_fmaf(__builtin_fmaxf(mx[0], mx[1]), c_log2, lin0),
-                             __builtin_fmaf(__builtin_fmaxf(mx[2], mx[3]), c_log2, lin1));
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+        tmax = __builtin_fmaxf(tmax, __builtin_fmaf(__builtin_fmaxf(mx[2 * kb], mx[2 * kb + 1]), c_log2, lin[kb]));
     } else {
-      tmax = __builtin_fmaxf(__builtin_fmaxf(mx[0], mx[1]), __builtin_fmaxf(mx[2], mx[3]));
+#pragma unroll
+      for (int kb = 0; kb < C::KB; kb += 2)
+        tmax = __builtin_fmaxf(tmax, __builtin_fmaxf(__builtin_fmaxf(mx[2 * kb], mx[2 * kb + 1]),
+                                                     __builtin_fmaxf(mx[2 * kb + 2], mx[2 * kb + 3])));
       if constexpr (!GEN) tmax *= c_log2;
     }
     tmax = half_swap_max(tmax);
@@ -502,7 +520,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
       for (int i = 0; i < C::NDB; ++i) o[i] *= alpha;
     }
     const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
-    return f32x2{lin0 - mu, lin1 - mu};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) add[kb] = lin[kb] - mu;
   };
 
   // Tail of the softmax: P = 2^(x - mu) and O^T += V^T P^T (V in buffer
@@ -514,10 +533,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // whole chunk early, and scheduling barriers keep the compiler from
   // sinking them back next to their MFMAs (measured 4-8% faster than reads
   // placed by the scheduler).
-  auto softmax_tail = [&](auto with_s, f32x16 (&s)[2], f32x2 add, const char *vt, f32x16 (&sn)[2],
-                          const char *kt) __attribute__((always_inline)) {
+  auto softmax_tail = [&](auto with_s, f32x16 (&s)[C::KB], const float (&add)[C::KB], const char *vt,
+                          f32x16 (&sn)[C::KB], const char *kt) __attribute__((always_inline)) {
     constexpr bool WITH_S = decltype(with_s)::value;
-    constexpr int S_PER_CHUNK = 2 * C::NDC / 4;       // S MFMAs per 16-key chunk
+    constexpr int S_PER_CHUNK = C::KB * C::NDC / C::NCH;   // S MFMAs per 16-key chunk
     const char *vbase = vt + v_rd;
     const char *kbase = kt + k_rd;
     float ps[4];   // independent partial row sums, seeded by the first chunk
@@ -532,11 +551,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
       for (int t = 0; t < S_PER_CHUNK; ++t) kf[0][t] = k_frag(t);
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < C::NCH; ++c) {
       // Reads first: the next chunk's K fragments and this chunk's V^T.
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (WITH_S) {
-        if (c + 1 < 4) {
+        if (c + 1 < C::NCH) {
 #pragma unroll
           for (int t = 0; t < S_PER_CHUNK; ++t) kf[(c + 1) & 1][t] = k_frag((c + 1) * S_PER_CHUNK + t);
         }
@@ -595,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // ---- prologue: K0, V0, K1 (and the document ids of tiles 0, 1)
   // resident; S0 computed.  Tile n uses K and V buffer n % 2 and document
   // slot n % 3.
-  f32x16 sa[2], sb[2];
+  f32x16 sa[C::KB], sb[C::KB];
   if (n_tiles > 0) {
     load_k(k_lds0, tile_key0(0));
     load_v(v_lds0, tile_key0(0));
@@ -626,7 +645,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // (2) softmax of tile n with its P·V MFMAs (V tile v_cur), interleaved with
   // the S MFMAs of tile n+1 (K tile k_next); (3) store the ids into the slot
   // tile n-1 freed, wait for this wave's loads, barrier.
-  auto iteration = [&](int n, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], char *k_fill, char *v_fill,
+  auto iteration = [&](int n, f32x16 (&s_cur)[C::KB], f32x16 (&s_next)[C::KB], char *k_fill, char *v_fill,
                        const char *v_cur, const char *k_next) __attribute__((always_inline)) {
     const int k0 = tile_key0(n);
     int doc_fill = 0;
@@ -646,7 +665,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
       // this wave (a dead or absent tile reads a stale, valid K buffer and
       // the result is never used): one code path keeps the whole tail in a
       // single scheduling region.
-      const f32x2 add = softmax_head(s_cur, k0, n, n % 3);
+      float add[C::KB];
+      softmax_head(s_cur, k0, n, n % 3, add);
       // The tail (exp2, P·V and the next tile's S on the matrix cores) runs
       // at raised wave priority, so a wave there issues ahead of waves in
       // their softmax head or waiting on loads: measured 6-7% faster on

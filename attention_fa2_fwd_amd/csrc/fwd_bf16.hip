@@ -632,7 +632,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   for (int c = 0; c < C::NDC; ++c) asm volatile("" ::"v"(qf[c]));
   if (n_tiles > 0) __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0)
   __syncthreads();
-  if (n_tiles > 0 && !tile_empty(tile_key0(0), 0)) compute_s(sa, k_lds0);
+  // The first key and liveness of the current tile and the first key of the
+  // next are carried from one iteration to the next, so an iteration reads
+  // one new list entry (BlockMask) and classifies one new tile.
+  int key_cur = (n_tiles > 0) ? __builtin_amdgcn_readfirstlane(tile_key0(0)) : 0;
+  int key_nxt = (n_tiles > 1) ? __builtin_amdgcn_readfirstlane(tile_key0(1)) : 0;
+  bool live_cur = (n_tiles > 0) && !tile_empty(key_cur, 0);
+  if (live_cur) compute_s(sa, k_lds0);
   // Iteration 0 refills K buffer 0 (tile 2): every wave must be done reading
   // tile 0 from it first.  Later refills target a buffer last read before
   // the previous iteration's barrier.
@@ -647,19 +653,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // tile n-1 freed, wait for this wave's loads, barrier.
   auto iteration = [&](int n, f32x16 (&s_cur)[C::KB], f32x16 (&s_next)[C::KB], char *k_fill, char *v_fill,
                        const char *v_cur, const char *k_next) __attribute__((always_inline)) {
-    const int k0 = tile_key0(n);
+    const int k0 = key_cur;
+    const int k2 = (n + 2 < n_tiles) ? __builtin_amdgcn_readfirstlane(tile_key0(n + 2)) : 0;
     int doc_fill = 0;
     // The loads issue at raised priority too (measured 1-3% faster): only
     // the softmax head runs at the base priority.
     __builtin_amdgcn_s_setprio(1);
     if (n + 2 < n_tiles) {
-      if (DOC && wave == 0) doc_fill = load_doc(tile_key0(n + 2));
-      load_k(k_fill, tile_key0(n + 2));
+      if (DOC && wave == 0) doc_fill = load_doc(k2);
+      load_k(k_fill, k2);
     }
-    if (n + 1 < n_tiles) load_v(v_fill, tile_key0(n + 1));
+    if (n + 1 < n_tiles) load_v(v_fill, key_nxt);
     __builtin_amdgcn_s_setprio(0);
-    const bool cur_live = !tile_empty(k0, n % 3);
-    const bool next_live = (n + 1 < n_tiles) && !tile_empty(tile_key0(n + 1), (n + 1) % 3);
+    const bool cur_live = live_cur;
+    const bool next_live = (n + 1 < n_tiles) && !tile_empty(key_nxt, (n + 1) % 3);
+    live_cur = next_live;
+    key_cur = key_nxt;
+    key_nxt = k2;
     if (cur_live) {
       // The next tile's S is computed whether or not that tile is live for
       // this wave (a dead or absent tile reads a stale, valid K buffer and

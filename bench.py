@@ -418,12 +418,13 @@ def main():
                      "tflops_at_median": round(flops / (t["median_ms"] * 1e-3) / 1e12, 3)},
         "cpu_baseline": None,
         "prewarm": {"seconds": PREWARM_S, "launches": prewarm_launches,
-                    "why": "the timed steps run at the GPU's steady clocks"},
+                    "why": "the timed steps run at the GPU's steady clocks",
+                    "other_workloads": f"each pre-warmed {PREWARM_S} s the same way"},
     }
 
     # ---- paged decode roofline (HBM), 64 sequences
     print("[bench] paged decode", file=sys.stderr, flush=True)
-    dec = bench_decode(af, torch, workloads, 20, 3)
+    dec = bench_decode(af, torch, workloads, 20, 3, prewarm_s=PREWARM_S)
     dsrc = os.path.join(ROOT, "attention_fa2_fwd_amd", "csrc", "decode.hip")
     line["roofline_decode"] = {
         "bound": "hbm", "achieved": round(dec["GB_per_s"], 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -443,16 +444,17 @@ def main():
                          ("causal_softcap5", workloads.CAUSAL_SOFTCAP),
                          ("document_window1024_blockmask", workloads.DOC_WINDOW_BLOCKMASK)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
-            extra[name] = bench_prefill(af, torch, workloads, wl, 20, 3)
+            extra[name] = bench_prefill(af, torch, workloads, wl, 20, 3, prewarm_s=PREWARM_S)
         for name, wl in (("backward_causal_b4h16s2048d64", workloads.CAUSAL_BF16),
                          ("backward_gqa_window1024_alibi", workloads.GQA_WINDOW_ALIBI),
                          ("backward_document_blockmask", workloads.DOCUMENT_BLOCKMASK)):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
-            extra[name] = bench_backward(af, torch, workloads, wl, 10, 2)
+            extra[name] = bench_backward(af, torch, workloads, wl, 10, 2, prewarm_s=PREWARM_S)
         extra["paged_decode"] = dec
         print("[bench] paged decode, window 1024 + alibi", file=sys.stderr, flush=True)
         extra["paged_decode_window1024_alibi"] = bench_decode(af, torch, workloads, 20, 3,
-                                                              window=1024, score="alibi")
+                                                              window=1024, score="alibi",
+                                                              prewarm_s=PREWARM_S)
         line["workloads"] = {k2: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                                   for kk, vv in r.items()} for k2, r in extra.items()}
 

@@ -373,17 +373,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
+  // The current tile's first key and full flag are carried from the
+  // iteration that loaded it, so an iteration looks up one list entry.
+  int key_cur = (n_tiles > 0) ? __builtin_amdgcn_readfirstlane(tile_key0(0)) : 0;
+  bool flag_cur = (n_tiles > 0) && tile_flag(0);
   auto iteration = [&](int n, char *k_cur, char *v_cur, int32_t *d_cur, char *k_nxt, char *v_nxt,
                        int32_t *d_nxt) __attribute__((always_inline)) {
-    const int k0 = tile_key0(n);
+    const int k0 = key_cur;
+    const bool f0 = flag_cur;
     int doc_fill = 0;
     if (n + 1 < n_tiles) {
-      const int k1 = tile_key0(n + 1);
+      const int k1 = __builtin_amdgcn_readfirstlane(tile_key0(n + 1));
+      key_cur = k1;
+      flag_cur = tile_flag(n + 1);
       load_tile(k_nxt, k_rsrc, k1);
       load_tile(v_nxt, v_rsrc, k1);
       if (DOC && wave == 0) doc_fill = load_doc(k1);
     }
-    if (n < n_tiles) tile_step(k0, tile_flag(n), k_cur, v_cur, d_cur);
+    if (n < n_tiles) tile_step(k0, f0, k_cur, v_cur, d_cur);
     if (DOC && wave == 0 && n + 1 < n_tiles) d_nxt[lane] = doc_fill;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -552,14 +559,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   auto tile_flag = [&](int t) __attribute__((always_inline)) -> bool {
     return use_bm && s_qfull[t >> 2] != 0;
   };
-  auto load_tiles = [&](Step st, char *qd, char *od) __attribute__((always_inline)) {
+  auto load_tiles = [&](Step st, int q0, char *qd, char *od) __attribute__((always_inline)) {
     const int hq = st.hq;
     const size_t base = ((size_t)(b * a.Hq + hq) * a.Sq) * D;
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.q + base), (short)0, a.Sq * D * 2, kBufferFlags);
     const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.dout + base), (short)0, a.Sq * D * 2, kBufferFlags);
-    const int soff = __builtin_amdgcn_readfirstlane(tile_q0(st.t) * D * 2);
+    const int soff = __builtin_amdgcn_readfirstlane(q0 * D * 2);
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)(qd + (4 * i + wave) * T::BLK), 16,
@@ -574,8 +581,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     float lse2, dot;
     int doc;
   };
-  auto fetch_qvals = [&](Step st) __attribute__((always_inline)) -> QVals {
-    const int i = tile_q0(st.t) + lane;
+  auto fetch_qvals = [&](Step st, int q0) __attribute__((always_inline)) -> QVals {
+    const int i = q0 + lane;
     QVals r{INFINITY, 0.0f, -1};
     if (lane < kQTile && i < a.Sq) {
       const size_t row = (size_t)(b * a.Hq + st.hq) * a.Sq + i;
@@ -597,12 +604,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int tr_j = lane & 15;
   const int rd_tr = T::off(4 * h + (tr_j >> 2)) + (16 * ((lane >> 4) & 1) + 4 * (tr_j & 3)) * 2;
 
-  auto tile_step = [&](Step st, const char *qt_, const char *ot, const float *ls, const float *dt,
+  auto tile_step = [&](Step st, int i0, bool flag, const char *qt_, const char *ot, const float *ls,
+                       const float *dt,
                        const int32_t *dc) __attribute__((always_inline)) {
-    const int i0 = tile_q0(st.t);
     const int i1 = i0 + kQTile - 1;
     if (jw0 >= a.Skv || i0 >= a.Sq || block_empty<MASK>(a.mask, i0, i1, jw0, jw1)) return;
-    const bool full = tile_flag(st.t) || block_full<MASK>(a.mask, i0, i1, jw0, jw1);
+    const bool full = flag || block_full<MASK>(a.mask, i0, i1, jw0, jw1);
     const int hq = st.hq;
     const float bias2 = (MOD == kModAdd) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
     // S = Q K^T and dP = dO V^T for the 32 queries: element r is query
@@ -677,23 +684,32 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
   const Step first{hkv * G, 0};
   if (n_iter > 0) {
-    load_tiles(first, q_lds0, o_lds0);
-    if (wave == 0) store_qvals(fetch_qvals(first), qv_lse0, qv_dot0, qv_doc0);
+    load_tiles(first, tile_q0(first.t), q_lds0, o_lds0);
+    if (wave == 0) store_qvals(fetch_qvals(first, tile_q0(first.t)), qv_lse0, qv_dot0, qv_doc0);
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
+  // The current step's first query and full flag are carried from the
+  // iteration that loaded it, so an iteration looks up one list entry.
+  int q0_cur = (n_iter > 0) ? __builtin_amdgcn_readfirstlane(tile_q0(first.t)) : 0;
+  bool flag_cur = (n_iter > 0) && tile_flag(first.t);
   // Iteration it (step st): load step it + 1 into the buffers step it - 1
   // used, compute step it, wait for this wave's loads, barrier.
   auto iteration = [&](int it, Step st, char *q_cur, char *o_cur, float *l_cur, float *d_cur,
                        int32_t *c_cur, char *q_nxt, char *o_nxt, float *l_nxt, float *d_nxt,
                        int32_t *c_nxt) __attribute__((always_inline)) {
+    const int i0 = q0_cur;
+    const bool f0 = flag_cur;
     QVals nv{INFINITY, 0.0f, -1};
     if (it + 1 < n_iter) {
       const Step nx = next_step(st);
-      load_tiles(nx, q_nxt, o_nxt);
-      if (wave == 0) nv = fetch_qvals(nx);
+      const int q1 = __builtin_amdgcn_readfirstlane(tile_q0(nx.t));
+      q0_cur = q1;
+      flag_cur = tile_flag(nx.t);
+      load_tiles(nx, q1, q_nxt, o_nxt);
+      if (wave == 0) nv = fetch_qvals(nx, q1);
     }
-    if (it < n_iter) tile_step(st, q_cur, o_cur, l_cur, d_cur, c_cur);
+    if (it < n_iter) tile_step(st, i0, f0, q_cur, o_cur, l_cur, d_cur, c_cur);
     if (wave == 0 && it + 1 < n_iter) store_qvals(nv, l_nxt, d_nxt, c_nxt);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

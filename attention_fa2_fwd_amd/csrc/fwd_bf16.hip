@@ -12,9 +12,9 @@
 //
 // Layout of the work (CDNA4-specific choices):
 //  * workgroup = 256 threads = 4 wave64s, 128 query rows; each wave owns 32
-//    consecutive rows.  Key tiles of 64 rows.  Two workgroups per CU, so
-//    each SIMD interleaves two waves: one's MFMAs run beside the other's
-//    softmax.
+//    consecutive rows.  Key tiles of 64 rows (128 for unmasked D=64).  Two
+//    workgroups per CU, so each SIMD interleaves two waves: one's MFMAs run
+//    beside the other's softmax.
 //  * Scores are computed transposed, S^T = K·Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand, Q^T (kept in
 //    VGPRs for the whole kernel) the B operand.  In the 32x32 accumulator
@@ -444,7 +444,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-          s[kb][r] = ((unsigned)(hi - off) < span) ? s[kb][r] : -INFINITY;
+          if constexpr (WIN) s[kb][r] = ((unsigned)(hi - off) < span) ? s[kb][r] : -INFINITY;
+          else s[kb][r] = (off <= hi) ? s[kb][r] : -INFINITY;   // lo = 0: one compare with a constant
         }
     }
     if (!full && DOC) {
@@ -486,9 +487,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2)
-        mx[2 * kb + ((r >> 1) & 1)] =
-            __builtin_fmaxf(mx[2 * kb + ((r >> 1) & 1)], __builtin_fmaxf(s[kb][r], s[kb][r + 1]));
+      for (int r = 0; r < 16; r += 2) {
+        // One v_max3 folds two scores into a partial max (the compiler's own
+        // tree used 24 max ops for 32 scores; this is 16): +2-3% on causal
+        // and soft-cap D=64, neutral elsewhere, same results.
+        float &m = mx[2 * kb + ((r >> 1) & 1)];
+        asm("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(m), "v"(s[kb][r]), "v"(s[kb][r + 1]));
+      }
     // kModLin: the bias of element r of block kb is bias2 (jb + 32 kb - qi)
     // plus the part already in the accumulator.
     float lin[C::KB];

@@ -90,6 +90,15 @@ def test_bf16_rectangular(Sq, Skv, mask):
     run_case(1, 2, 1, Sq, Skv, 128, "bf16", mask, "alibi", seed=Sq + Skv)
 
 
+# Unmasked D=64 runs on 128-key tiles, so its ragged ends and short key
+# ranges get shapes of their own (the tile's last key past Skv, Skv < 128,
+# Skv a multiple of 128, one query).
+@pytest.mark.parametrize("Sq,Skv", [(200, 333), (333, 200), (64, 1000), (1, 77), (129, 256), (300, 127)])
+@pytest.mark.parametrize("score", ["none", "alibi", "softcap"])
+def test_bf16_rectangular_unmasked_d64(Sq, Skv, score):
+    run_case(2, 4, 2, Sq, Skv, 64, "bf16", "none", score, seed=Sq + 3 * Skv)
+
+
 @pytest.mark.parametrize("D", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("mask", MASKS)
 def test_f32_small(D, mask):
@@ -139,14 +148,16 @@ def test_tiny_causal_f32_workload():
     run_case(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.dtype, w.mask, w.score, seed=w.seed)
 
 
-@pytest.mark.parametrize("mask", ["causal", "sliding", "prefix_lm", "document", "sliding&document&causal"])
-def test_block_mask_path_equals_dense_path(mask):
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "sliding", "prefix_lm", "document", "sliding&document&causal"])
+def test_block_mask_path_equals_dense_path(D, mask):
     """The BlockMask-driven kernel matches the oracle and, bit for bit, the
-    analytic-range kernel (the same tiles hold the same visible keys)."""
-    out_bm, lse_bm = run_case(1, 4, 4, 700, 700, 128, "bf16", mask, "none", seed=5,
+    analytic-range kernel (the same tiles hold the same visible keys).  At
+    D=64 without a mask a 128-key block is one tile."""
+    out_bm, lse_bm = run_case(1, 4, 4, 700, 700, D, "bf16", mask, "none", seed=5,
                               window=200, prefix_len=150, doc_lengths=(300, 41, 129, 230),
                               block_mask=True)
-    out_d, lse_d = run_case(1, 4, 4, 700, 700, 128, "bf16", mask, "none", seed=5,
+    out_d, lse_d = run_case(1, 4, 4, 700, 700, D, "bf16", mask, "none", seed=5,
                             window=200, prefix_len=150, doc_lengths=(300, 41, 129, 230))
     assert torch.equal(out_bm, out_d)
     assert torch.equal(lse_bm, lse_d)

@@ -53,7 +53,6 @@ constexpr int kKTile = 64;         // key rows per tile in the dQ kernel
 constexpr int kKRows = 128;        // keys per dK/dV workgroup
 constexpr int kQTile = 32;         // query rows per tile in the dK/dV kernel
 constexpr int kListCap = 1024;     // BlockMask entries staged in LDS (host-checked)
-static_assert(2 * kOrderCap <= kListCap, "work-ordering scratch fits the list buffer");
 // Score forms: raw scores, a bias added, or the soft cap.
 constexpr int kModAdd = 0, kModCap = 1, kModRaw = 2;
 
@@ -177,14 +176,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
   // Longest key ranges first: the later query tiles, or with a BlockMask the
-  // tiles with the most listed blocks (ranked in the list buffer before the
-  // list is staged).
+  // tiles with the most listed blocks (each wave ranks the counts itself).
   const int pos = (int)(blockIdx.x / bh_count);
   int qt = n_qtiles - 1 - pos;
   if (a.bm_num && n_qtiles <= kOrderCap) {
     const int bb = (a.bm_batch == 1) ? 0 : b;
-    qt = work_ordered_tile(a.bm_num + (size_t)bb * a.bm_nqb, n_qtiles, min(a.bm_nkb, kListCap), pos, true,
-                           s_blk, tid, kThreads);
+    qt = work_ordered_tile(a.bm_num + (size_t)bb * a.bm_nqb, n_qtiles, min(a.bm_nkb, kListCap), pos, true);
   }
   const int hkv = (hq * a.Hkv) / a.Hq;
   const int q0 = qt * kQRows;
@@ -453,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int hkv = bh - b * a.Hkv;
   // Most query tiles first: the first key tiles, or with a BlockMask the key
   // blocks with the most listed query blocks (ties, the earlier block first;
-  // ranked in the list buffer before the list is staged).
+  // each wave ranks the counts itself).
   const int pos = (int)(blockIdx.x / bh_count);
   int kt = pos;
   if (a.bm_num && a.bm_qnum) {
@@ -461,7 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     if (n_ktiles <= kOrderCap) {
       const int bb = (a.bm_batch == 1) ? 0 : b;
       kt = work_ordered_tile(a.bm_qnum + (size_t)bb * a.bm_nkb, n_ktiles, min(a.bm_nqb, kListCap), pos,
-                             false, s_qblk, tid, kThreads);
+                             false);
     }
   }
   const int G = a.Hq / a.Hkv;

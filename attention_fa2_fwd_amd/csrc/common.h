@@ -116,38 +116,58 @@ __device__ __forceinline__ float half_swap_sum(float v) {
 
 // Work-ordered dispatch for launches whose tiles come from BlockMask lists:
 // a tile's work is its listed block count, which need not follow the tile
-// index (documents).  Every workgroup of the launch ranks the same counts and
-// takes the tile at its dispatch position pos, in the order: descending count
-// (clamped to [0, cap], cap < 2^15), ties by tile index, the later tile first
-// when later_first.  The sort keys (count << 16 | tie) are distinct, so the
-// ranks form one permutation, identical in every workgroup.  Needs
-// n <= kOrderCap and 2 * kOrderCap ints of 16-byte aligned LDS scratch; every
-// thread of the workgroup calls it (it holds barriers).
+// index (documents).  Every wave of the launch orders the same counts and
+// takes the tile at its dispatch position pos (0 <= pos < n), in the order:
+// descending count (clamped to [0, cap], cap < 2^15), ties by tile index, the
+// later tile first when later_first.  That is one permutation of the n
+// tiles, the same in every wave.  Each wave finds its tile on its own, with
+// no LDS and no barrier: the counts (n <= kOrderCap, four per lane) go into
+// registers; a binary search over count values finds v, the count of the
+// tile at pos (the largest v with more than pos tiles counting at least v);
+// and lane prefix counts over the ballot of the tiles of count v pick the
+// one at rank pos - #(count > v) among them.  With count set, v is returned
+// there too, so the caller need not read the tile's count again.
 constexpr int kOrderCap = 256;
 __device__ inline int work_ordered_tile(const int32_t *cnt, int n, int cap, int pos, bool later_first,
-                                        int32_t *scratch, int tid, int nthreads) {
-  int32_t *s_key = scratch;
-  int32_t *s_order = scratch + kOrderCap;
-  const int n4 = (n + 3) & ~3;   // keys padded with INT_MIN to whole int4s
-  for (int t = tid; t < n4; t += nthreads) {
-    const int tie = later_first ? t : kOrderCap - 1 - t;
-    s_key[t] = (t < n) ? (min(max(cnt[t], 0), cap) << 16) | tie : INT_MIN;
+                                        int *count = nullptr) {
+  constexpr int KPL = kOrderCap / 64;
+  const int lane = threadIdx.x & 63;
+  int c[KPL];   // clamped counts of tiles lane + 64 j; -1 past n
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int t = lane + 64 * j;
+    c[j] = (t < n) ? min(max(cnt[t], 0), cap) : -1;
   }
-  __syncthreads();
-  for (int t = tid; t < n; t += nthreads) {
-    const int key = s_key[t];
-    int r = 0;
-#pragma unroll 4
-    for (int u = 0; u < n4; u += 4) {
-      const int4 v = *(const int4 *)&s_key[u];
-      r += (int)(v.x > key) + (int)(v.y > key) + (int)(v.z > key) + (int)(v.w > key);
-    }
-    s_order[r] = t;
+  auto count_ge = [&](int v) -> int {   // tiles whose count is at least v
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) s += __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[j] >= v));
+    return s;
+  };
+  int lo = 0, hi = cap;   // count_ge(lo) > pos holds from the start: count_ge(0) = n
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (count_ge(mid) > pos) lo = mid;
+    else hi = mid - 1;
   }
-  __syncthreads();
-  const int tile = s_order[pos];
-  __syncthreads();   // scratch is free again for the caller
-  return tile;
+  const int v = lo;
+  const int k = pos - count_ge(v + 1);   // rank among the tiles of count v
+  int sel = 0;
+  int ahead = 0;   // tiles of count v in the lane blocks already passed
+#pragma unroll
+  for (int jj = 0; jj < KPL; ++jj) {
+    const int j = later_first ? KPL - 1 - jj : jj;
+    const bool mine = (c[j] == v);
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(mine);
+    const int pc = __builtin_popcountll(m);
+    const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+    const int r = ahead + (later_first ? pc - 1 - below : below);
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(mine && r == k);
+    if (hit) sel = 64 * j + __builtin_ctzll(hit);
+    ahead += pc;
+  }
+  if (count) *count = v;
+  return sel;
 }
 
 // Minimum / maximum of an int over the 64 lanes of a wave, in every lane, by

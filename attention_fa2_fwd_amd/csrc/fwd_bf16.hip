@@ -66,7 +66,6 @@ constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kMaskBlock = 128;
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kListCap = 1024; // BlockMask entries staged in LDS per query tile (host-checked)
-static_assert(2 * kOrderCap <= kListCap, "work-ordering scratch fits the list buffer");
 // Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kKPad = 16;      // bytes between K row blocks
@@ -180,16 +179,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // Heaviest query tiles first.  Without a BlockMask the later tiles are the
   // heavier ones (causal-type masks give them more keys).  With one, a tile's
   // work is its listed block count, which need not grow with the tile index
-  // (documents): every workgroup ranks the tiles of its batch row by count
+  // (documents): every wave ranks the tiles of its batch row by count
   // (descending; ties, the later tile first) and takes the tile at its
-  // dispatch position (the ranking's scratch is the list buffer, free until
-  // the list is staged).
+  // workgroup's dispatch position.
   const int pos = (int)(blockIdx.x / bh_count);
   int qt = a.n_qtiles - 1 - pos;
+  int n_ranked = -1;   // the tile's clamped list length, when the ranking ran
   if (a.bm_num && a.n_qtiles <= kOrderCap) {
     const int bb = (a.bm_batch == 1) ? 0 : b;
     qt = work_ordered_tile(a.bm_num + (size_t)bb * a.bm_nqb, a.n_qtiles, min(a.bm_nkb, kListCap), pos,
-                           true, s_blk, tid, kThreads);
+                           true, &n_ranked);
   }
   const int hkv = (hq * a.Hkv) / a.Hq;
   const int q0 = qt * kBM;
@@ -199,12 +198,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
 
   const size_t q_base = ((size_t)(b * a.Hq + hq) * a.Sq) * D;
   const size_t kv_base = ((size_t)(b * a.Hkv + hkv) * a.Skv) * D;
+  // The row's document id is fetched now, so its latency overlaps the
+  // BlockMask list's (it is waited for after the list is staged).
+  const int32_t *doc_row = DOC ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride : nullptr;
+  const int doc_i = DOC ? doc_row[min(qi, a.Sq - 1)] : 0;
 
   // Q^T fragments: lane holds Q[qi][16c + 8h .. 16c + 8h + 7] (rows past Sq
   // read row Sq-1 and are never stored).  Loaded in the prologue, after the
   // first tile loads are issued, so the two latencies overlap.
   bf16x8 qf[C::NDC];
   const bf16x8 *q_src = (const bf16x8 *)(a.q + q_base + (size_t)min(qi, a.Sq - 1) * D);
+#pragma unroll
+  for (int c = 0; c < C::NDC; ++c) qf[c] = q_src[2 * c + h];
 
   // ---- key tiles to visit.  A BlockMask row is staged in LDS so the tile
   // loop reads it without vector memory waits (the host limits a row to
@@ -219,13 +224,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     const size_t row = (size_t)bb * a.bm_nqb + qt;
     // Counts and indices are device data: clamp them so a malformed list
     // can only drop tiles, never address outside K/V.
-    const int n_blocks = min(max(a.bm_num[row], 0), min(a.bm_nkb, kListCap));
+    int n_blocks = __builtin_amdgcn_readfirstlane(n_ranked);
+    if (n_blocks < 0) n_blocks = min(max(a.bm_num[row], 0), min(a.bm_nkb, kListCap));
     n_tiles = n_blocks * C::TPB;
     bm_list = a.bm_idx + row * a.bm_nkb;
     if (a.bm_full) bm_flags = a.bm_full + row * a.bm_nkb;
-    for (int t = tid; t < n_blocks; t += kThreads) {
-      s_blk[t] = bm_list[t];
-      s_full[t] = bm_flags ? bm_flags[t] : 0;
+    // Every load of the row (entries and flags, through range-checked
+    // buffer loads, so entries past n_blocks read as 0) is issued before the
+    // first store: one memory latency, shared with the Q and document-id
+    // loads issued above.
+    const __amdgpu_buffer_rsrc_t l_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)bm_list, (short)0, n_blocks * 4, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t f_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(bm_flags ? (const void *)bm_flags : (const void *)bm_list), (short)0, bm_flags ? n_blocks : 0,
+        kBufferFlags);
+    constexpr int kPer = kListCap / kThreads;
+    int32_t blk[kPer];
+    uint8_t full[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      if (u * kThreads < n_blocks) {   // wave-uniform
+        blk[u] = __builtin_amdgcn_raw_buffer_load_b32(l_rsrc, (tid + u * kThreads) * 4, 0, 0);
+        full[u] = __builtin_amdgcn_raw_buffer_load_b8(f_rsrc, tid + u * kThreads, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int t = tid + u * kThreads;
+      if (t < n_blocks) {
+        s_blk[t] = blk[u];
+        s_full[t] = full[u];
+      }
     }
     __syncthreads();   // the list is read by every wave from here on
   } else {
@@ -261,8 +290,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     const int bi = n >> C::TPB_SHIFT;
     return s_full[bi] != 0;
   };
-
-  const int32_t *doc_row = DOC ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride : nullptr;
 
   // ---- HBM/L2 -> LDS through buffer_load ... lds.  Wave w, load i fills
   // row block blk = 4i + w: lane L writes bytes [16L, 16L + 16) of the block,
@@ -336,7 +363,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // Soft cap in log2 units and its exponent factor (2 / cap) * c.
   const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
   const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
-  const int doc_i = DOC ? doc_row[min(qi, a.Sq - 1)] : 0;
   asm volatile("" ::"v"(doc_i));   // complete the load before the tile loop
   // Range of the wave's row ids (rows past Sq repeat row Sq - 1): a key tile
   // whose id range misses it holds no visible key for the wave, and one
@@ -621,18 +647,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // slot n % 3.
   f32x16 sa[C::KB], sb[C::KB];
   if (n_tiles > 0) {
+    // The document ids go first: their stores then wait for them alone,
+    // not for the tile loads issued after them.
+    int d0 = 0, d1 = 0;
+    if (DOC && wave == 0) {
+      d0 = load_doc(tile_key0(0));
+      if (n_tiles > 1) d1 = load_doc(tile_key0(1));
+    }
     load_k(k_lds0, tile_key0(0));
     load_v(v_lds0, tile_key0(0));
     if (n_tiles > 1) load_k(k_lds1, tile_key0(1));
     if (DOC && wave == 0) {
-      store_doc(0, load_doc(tile_key0(0)));
-      if (n_tiles > 1) store_doc(1, load_doc(tile_key0(1)));
+      store_doc(0, d0);
+      if (n_tiles > 1) store_doc(1, d1);
     }
   }
   // The empty asm statements make the Q loads complete here, so the tile
   // loop never waits on them.
-#pragma unroll
-  for (int c = 0; c < C::NDC; ++c) qf[c] = q_src[2 * c + h];
 #pragma unroll
   for (int c = 0; c < C::NDC; ++c) asm volatile("" ::"v"(qf[c]));
   if (n_tiles > 0) __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0)

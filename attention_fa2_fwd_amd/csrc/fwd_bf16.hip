@@ -101,7 +101,8 @@ struct KernelArgs {
   void *out;           // bf16 or fp32 [B, Hq, Sq, D]
   float *lse;
   int B, Hq, Hkv, Sq, Skv;
-  int n_qtiles;
+  int n_qtiles;        // query tiles per (b, head unit): ceil(Sq / rows per workgroup)
+  int gqa_pack;        // 1: a workgroup is 32 positions of four query heads (see the kernel)
   float scale_log2;    // scale * log2(e)
   MaskArgs mask;
   ScoreArgs score;
@@ -169,13 +170,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   const int h = lane >> 5;      // lane half: selects keys 4h..4h+3 of each 8
   const int l32 = lane & 31;    // query column of this lane
 
+  // What a workgroup covers.  By default one query head and 128 consecutive
+  // query rows, wave w taking rows 32w .. 32w + 31.  With gqa_pack (grouped
+  // heads, Hq / Hkv a multiple of 4, no BlockMask) it covers 32 query
+  // positions of four query heads that share a kv head, wave w taking head
+  // 4g + w: every wave then needs the same key tiles, so the workgroup visits
+  // the key range of 32 rows instead of the union of four staggered ones (a
+  // 1024-key window spans 17 tiles of 64 keys instead of 18), and no wave
+  // sits out a tile its neighbours compute.
   // Workgroups go round-robin to the 8 XCDs; each XCD gets a contiguous run
-  // of heads, so the query heads of one kv head share an L2.
-  const int bh_count = a.B * a.Hq;
+  // of head units, so the query heads of one kv head share an L2.
+  const int pack = a.gqa_pack;
+  const int hunits = pack ? a.Hq / 4 : a.Hq;   // head units per batch row
+  const int bh_count = a.B * hunits;
   const int xh = (int)(blockIdx.x % bh_count);
   const int bh = (bh_count % 8 == 0) ? (xh % 8) * (bh_count / 8) + xh / 8 : xh;
-  const int b = bh / a.Hq;
-  const int hq = bh - b * a.Hq;
+  const int b = bh / hunits;
+  const int hu = bh - b * hunits;
+  const int hq = pack ? 4 * hu + wave_s : hu;   // wave-uniform
   // Heaviest query tiles first.  Without a BlockMask the later tiles are the
   // heavier ones (causal-type masks give them more keys).  With one, a tile's
   // work is its listed block count, which need not grow with the tile index
@@ -191,8 +203,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
                            true, &n_ranked);
   }
   const int hkv = (hq * a.Hkv) / a.Hq;
-  const int q0 = qt * kBM;
-  const int qw0 = q0 + wave * 32;
+  const int rows = pack ? 32 : kBM;   // query positions per workgroup
+  const int q0 = qt * rows;
+  const int qw0 = pack ? q0 : q0 + wave * 32;
   const int qw1 = min(qw0 + 31, a.Sq - 1);
   const int qi = qw0 + l32;
 
@@ -214,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
   // ---- key tiles to visit.  A BlockMask row is staged in LDS so the tile
   // loop reads it without vector memory waits (the host limits a row to
   // kListCap entries).
-  const int qlast = min(q0 + kBM, a.Sq) - 1;
+  const int qlast = min(q0 + rows, a.Sq) - 1;
   int n_tiles;
   int t_first = 0;
   const int32_t *bm_list = nullptr;
@@ -800,7 +813,11 @@ hipError_t launch_d(const FwdParams &p, hipStream_t stream) {
   a.Hkv = p.Hkv;
   a.Sq = p.Sq;
   a.Skv = p.Skv;
-  a.n_qtiles = (p.Sq + kBM - 1) / kBM;
+  // Grouped heads in fours when the analytic key range applies (a BlockMask
+  // row covers 128 query rows, so BlockMask launches keep the 128-row tile).
+  a.gqa_pack = (p.bm_num == nullptr && p.Hkv > 0 && (p.Hq / p.Hkv) % 4 == 0) ? 1 : 0;
+  const int rows = a.gqa_pack ? 32 : kBM;
+  a.n_qtiles = (p.Sq + rows - 1) / rows;
   a.scale_log2 = p.scale * kLog2e;
   a.mask = p.mask;
   a.score = p.score;
@@ -810,7 +827,7 @@ hipError_t launch_d(const FwdParams &p, hipStream_t stream) {
   a.bm_nqb = p.bm_nqb;
   a.bm_nkb = p.bm_nkb;
   a.bm_batch = p.bm_batch;
-  const unsigned grid = (unsigned)(a.n_qtiles * p.B * p.Hq);
+  const unsigned grid = (unsigned)(a.n_qtiles * p.B * (a.gqa_pack ? p.Hq / 4 : p.Hq));
   if (p.score.kind == ATTN_SCORE_SOFTCAP) {
     return p.out_f32 ? launch_mask<D, kModCap, true>(a, p.mask.kind, grid, stream)
                      : launch_mask<D, kModCap, false>(a, p.mask.kind, grid, stream);

@@ -32,7 +32,7 @@ def oracle_specs(mask, score, window=0, prefix_len=0, doc_ids=None, rel_scale=1.
 
 def run_case(B, Hq, Hkv, Sq, Skv, D, dtype, mask, score, seed=0, window=100, prefix_len=70,
              doc_lengths=(50, 130, 7, 113), rel_scale=-0.05, block_mask=False, softcap=1.5,
-             scale=None):
+             scale=None, mha_equal=False):
     label = (f"B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Skv{Skv} D{D} {dtype} {mask} {score} bm={block_mask}"
              f" scale={scale} softcap={softcap if score == 'softcap' else '-'}")
     q, k, v = workloads.randn_qkv(B, Hq, Hkv, Sq, Skv, D, dtype, seed)
@@ -53,6 +53,15 @@ def run_case(B, Hq, Hkv, Sq, Skv, D, dtype, mask, score, seed=0, window=100, pre
     kw = dict(scale=scale, mask=mask, window=window, prefix_len=prefix_len, doc_ids=dd,
               score=score, rel_scale=rel_scale, softcap=softcap, block_mask=bm)
     out, lse = af.attn_fwd(qd, kd, vd, **kw)
+    if mha_equal:
+        # The same launch with every query head given its own copy of its kv
+        # head: grouped heads (the four-head workgroups included) must give
+        # the multi-head result bit for bit.
+        g = Hq // Hkv
+        o_m, l_m = af.attn_fwd(qd, kd.repeat_interleave(g, dim=1).contiguous(),
+                               vd.repeat_interleave(g, dim=1).contiguous(), **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_m) and torch.equal(lse, l_m), label + " grouped != multi-head"
     out32 = None
     if q.dtype == torch.bfloat16:
         out32, lse32 = af.attn_fwd(qd, kd, vd, out_dtype=torch.float32, **kw)
@@ -161,6 +170,30 @@ def test_block_mask_path_equals_dense_path(D, mask):
                             window=200, prefix_len=150, doc_lengths=(300, 41, 129, 230))
     assert torch.equal(out_bm, out_d)
     assert torch.equal(lse_bm, lse_d)
+
+
+# Groups of four or more query heads per kv head run as workgroups of 32
+# positions of four heads each (no BlockMask): ragged position tiles (300 =
+# 9 * 32 + 12), one query, rectangular shapes, groups of 4 and 8, a head
+# count whose units do not fill the 8 XCDs evenly (12 heads), every mask kind
+# and score form.
+GQA_PACK_MASKS = ["none", "causal", "sliding", "prefix_lm", "document", "sliding&document&causal"]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", GQA_PACK_MASKS)
+@pytest.mark.parametrize("score", ["none", "alibi", "softcap"])
+def test_bf16_gqa_four_head_workgroups(D, mask, score):
+    run_case(1, 8, 2, 300, 300, D, "bf16", mask, score, seed=D + 7 * len(mask) + len(score),
+             window=77, mha_equal=True)
+
+
+@pytest.mark.parametrize("Hq,Hkv,Sq,Skv", [(8, 1, 200, 333), (12, 3, 333, 200), (16, 4, 1, 77),
+                                           (8, 2, 64, 1000), (12, 3, 130, 130)])
+@pytest.mark.parametrize("mask", ["none", "causal", "sliding"])
+def test_bf16_gqa_four_head_workgroups_shapes(Hq, Hkv, Sq, Skv, mask):
+    run_case(2, Hq, Hkv, Sq, Skv, 128, "bf16", mask, "alibi", seed=Sq + Skv + Hq, window=150,
+             mha_equal=True)
 
 
 def test_deterministic_and_gqa_equals_mha():

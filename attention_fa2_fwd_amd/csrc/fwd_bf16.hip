@@ -749,8 +749,39 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
 
   // ---- epilogue: O / l, LSE = (m + log2 l) ln 2.
   const float l_tot = half_swap_sum(l_run);
+  const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+  if constexpr (!OUT_F32) {
+    // The bf16 rows go out through LDS: each wave stages its 32 rows in one
+    // of the four tile buffers (free once the loop's last barrier has
+    // passed: every wave is done reading them and no load into them is in
+    // flight), then each store writes whole 16-byte chunks of 64 / (D / 8)
+    // full rows, 8 (D = 128) or 4 (D = 64) stores per lane instead of 16 or
+    // 8 scattered 8-byte ones.  The staging row stride of D * 2 + 16 bytes
+    // keeps both the 8-byte writes and the 16-byte reads free of bank
+    // conflicts.  Rows past Sq are staged but not stored.
+    constexpr int SROW = D * 2 + 16;
+    static_assert(32 * SROW <= C::KTILE && 32 * SROW <= C::VTILE, "a wave's rows fit one tile buffer");
+    char *stage = (wave_s == 0) ? k_lds0 : (wave_s == 1) ? k_lds1 : (wave_s == 2) ? v_lds0 : v_lds1;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 w = {pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
+                         pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+        *(u32x2 *)(stage + l32 * SROW + (32 * db + 8 * g + 4 * h) * 2) = w;
+      }
+    }
+    constexpr int CPR16 = D / 8;          // 16-byte chunks per row
+    constexpr int RPS = 64 / CPR16;       // rows per store
+    const int rr = lane / CPR16, cc = lane % CPR16;
+#pragma unroll
+    for (int i = 0; i < 32 / RPS; ++i) {
+      const int row = RPS * i + rr;
+      const u32x4 w = *(const u32x4 *)(stage + row * SROW + cc * 16);
+      if (qw0 + row < a.Sq) *(u32x4 *)((__bf16 *)a.out + q_base + (size_t)(qw0 + row) * D + cc * 8) = w;
+    }
+  }
   if (qi < a.Sq) {
-    const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
     if constexpr (OUT_F32) {
       float *orow = (float *)a.out + q_base + (size_t)qi * D;
 #pragma unroll
@@ -760,17 +791,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
           const f32x4 w = {o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv,
                            o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
           *(f32x4 *)(orow + 32 * db + 8 * g + 4 * h) = w;
-        }
-      }
-    } else {
-      __bf16 *orow = (__bf16 *)a.out + q_base + (size_t)qi * D;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 w = {pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
-                           pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-          *(u32x2 *)(orow + 32 * db + 8 * g + 4 * h) = w;
         }
       }
     }

@@ -179,9 +179,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   // tiles with the most listed blocks (each wave ranks the counts itself).
   const int pos = (int)(blockIdx.x / bh_count);
   int qt = n_qtiles - 1 - pos;
+  int n_ranked = -1;   // the tile's clamped list length, when the ranking ran
   if (a.bm_num && n_qtiles <= kOrderCap) {
     const int bb = (a.bm_batch == 1) ? 0 : b;
-    qt = work_ordered_tile(a.bm_num + (size_t)bb * a.bm_nqb, n_qtiles, min(a.bm_nkb, kListCap), pos, true);
+    qt = work_ordered_tile(a.bm_num + (size_t)bb * a.bm_nqb, n_qtiles, min(a.bm_nkb, kListCap), pos, true,
+                           &n_ranked);
   }
   const int hkv = (hq * a.Hkv) / a.Hq;
   const int q0 = qt * kQRows;
@@ -193,48 +195,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const size_t q_base = ((size_t)(b * a.Hq + hq) * a.Sq) * D;
   const size_t kv_base = ((size_t)(b * a.Hkv + hkv) * a.Skv) * D;
 
-  // Q^T and dO^T fragments (B operands): lane holds X[qi][16c + 8h .. + 7].
-  bf16x8 qf[NDC], df[NDC];
+  // Q^T and dO^T fragments (B operands): lane holds X[qi][16c + 8h .. + 7];
+  // O the same way, for the row term below.
+  bf16x8 qf[NDC], df[NDC], of[NDC];
   {
     const bf16x8 *qs = (const bf16x8 *)(a.q + q_base + (size_t)qr * D);
     const bf16x8 *ds = (const bf16x8 *)(a.dout + q_base + (size_t)qr * D);
+    const bf16x8 *os = (const bf16x8 *)(a.out + q_base + (size_t)qr * D);
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
       qf[c] = qs[2 * c + h];
       df[c] = ds[2 * c + h];
+      of[c] = os[2 * c + h];
     }
   }
   const size_t row = (size_t)(b * a.Hq + hq) * a.Sq + qr;
-  const float lse2 = a.lse[row] * kLog2e;
-  // D = sum_d dO O over the row: each lane half holds every other 8-wide
-  // chunk of it.  Stored for the dK/dV kernel.
-  float dsum;
-  {
-    const bf16x8 *os = (const bf16x8 *)(a.out + q_base + (size_t)qr * D);
-    float part = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NDC; ++c) {
-      const bf16x8 o8 = os[2 * c + h];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)o8[e], (float)df[c][e], part);
-    }
-    dsum = part + __shfl_xor(part, 32);
-  }
-  if (h == 0 && qi < a.Sq) a.row_dot[row] = dsum;
-  const float c_log2 = a.scale_log2;
-  const float bias2 = (MOD == kModAdd) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
-  const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
-  const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
-  const float inv_cap2 = (MOD == kModCap) ? 1.0f / cap2 : 0.0f;
+  const float lse_row = a.lse[row];
   const int32_t *doc_row = DOC ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride : nullptr;
   const int doc_i = DOC ? doc_row[qr] : 0;
 
-  f32x16 acc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
-
   // Key tiles of the workgroup's rows: the BlockMask row of this 128-row
   // query block (two 64-key tiles per listed block), or a closed-form range.
+  // The row loads above are in flight while the list is staged: the two
+  // share one memory latency.
   const bool use_bm = a.bm_num != nullptr;
   int n_tiles = 0, t_first = 0;
   if (use_bm) {
@@ -242,12 +225,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     const size_t brow = (size_t)bb * a.bm_nqb + qt;
     // Counts and indices are device data: clamped, so a malformed list can
     // only drop tiles, never address outside K / V.
-    const int n_blocks = min(max(a.bm_num[brow], 0), min(a.bm_nkb, kListCap));
+    int n_blocks = __builtin_amdgcn_readfirstlane(n_ranked);
+    if (n_blocks < 0) n_blocks = min(max(a.bm_num[brow], 0), min(a.bm_nkb, kListCap));
     n_tiles = 2 * n_blocks;
-    for (int t = tid; t < n_blocks; t += kThreads) {
-      s_blk[t] = a.bm_idx[brow * a.bm_nkb + t];
-      s_full[t] = a.bm_full ? a.bm_full[brow * a.bm_nkb + t] : 0;
-    }
+    stage_list_row<kListCap, kThreads>(a.bm_idx + brow * a.bm_nkb,
+                                       a.bm_full ? a.bm_full + brow * a.bm_nkb : nullptr, n_blocks, s_blk,
+                                       s_full, tid);
     __syncthreads();
   } else {
     const int qlast = min(q0 + kQRows, a.Sq) - 1;
@@ -263,6 +246,30 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     t_first = lo / kKTile;
     n_tiles = (hi > lo) ? (hi + kKTile - 1) / kKTile - t_first : 0;
   }
+  const float lse2 = lse_row * kLog2e;
+  // D = sum_d dO O over the row: each lane half holds every other 8-wide
+  // chunk of it.  Stored for the dK/dV kernel.
+  float dsum;
+  {
+    float part = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)of[c][e], (float)df[c][e], part);
+    }
+    dsum = part + __shfl_xor(part, 32);
+  }
+  if (h == 0 && qi < a.Sq) a.row_dot[row] = dsum;
+  const float c_log2 = a.scale_log2;
+  const float bias2 = (MOD == kModAdd) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
+  const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
+  const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
+  const float inv_cap2 = (MOD == kModCap) ? 1.0f / cap2 : 0.0f;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+
   auto tile_key0 = [&](int n) __attribute__((always_inline)) -> int {
     if (use_bm) {
       const int blk = s_blk[n >> 1];
@@ -453,12 +460,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // each wave ranks the counts itself).
   const int pos = (int)(blockIdx.x / bh_count);
   int kt = pos;
+  int n_ranked = -1;   // the block's clamped list length, when the ranking ran
   if (a.bm_num && a.bm_qnum) {
     const int n_ktiles = (a.Skv + kKRows - 1) / kKRows;
     if (n_ktiles <= kOrderCap) {
       const int bb = (a.bm_batch == 1) ? 0 : b;
       kt = work_ordered_tile(a.bm_qnum + (size_t)bb * a.bm_nkb, n_ktiles, min(a.bm_nqb, kListCap), pos,
-                             false);
+                             false, &n_ranked);
     }
   }
   const int G = a.Hq / a.Hkv;
@@ -475,49 +483,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // past Skv repeat the last one); they are first read after the barrier
   // that follows the prologue's loads.
   bf16x8 kf[NDC];
+  constexpr int CPR = D / 8;
+  constexpr int VPL = 32 * CPR / 64;   // 16-byte V chunks per lane
+  bf16x8 vx[VPL];
   {
     const bf16x8 *ks = (const bf16x8 *)(a.k + kv_base + (size_t)kr * D);
 #pragma unroll
     for (int c = 0; c < NDC; ++c) kf[c] = ks[2 * c + h];
-    constexpr int CPR = D / 8;
 #pragma unroll
-    for (int t = 0; t < 32 * CPR / 64; ++t) {
+    for (int t = 0; t < VPL; ++t) {
       const int idx = 64 * t + lane;
       const int r = idx / CPR, ch = idx % CPR;
       const int key = min(jw0 + r, a.Skv - 1);
-      const bf16x8 x = *(const bf16x8 *)(a.v + kv_base + (size_t)key * D + 8 * ch);
-      *(bf16x8 *)(v_rows[wave] + r * VROW + 16 * ch) = x;
+      vx[t] = *(const bf16x8 *)(a.v + kv_base + (size_t)key * D + 8 * ch);
     }
   }
-  const char *vrow = v_rows[wave] + l32 * VROW + 16 * h;
-  const float c_log2 = a.scale_log2;
-  const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
-  const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
-  const float inv_cap2 = (MOD == kModCap) ? 1.0f / cap2 : 0.0f;
   const int32_t *doc_row = DOC ? a.mask.doc_ids + (size_t)b * a.mask.doc_stride : nullptr;
   const int doc_j = DOC ? doc_row[kr] : 0;
 
-  f32x16 dk[NDB], dv[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
-  }
-
   // Query tiles that may see the workgroup's keys [j0, jlast]: the
   // BlockMask column of this 128-key block (four 32-row tiles per listed
-  // query block), or a closed-form range.
+  // query block), or a closed-form range.  The K and V row loads above are
+  // in flight while the list is staged: the two share one memory latency.
   const bool use_bm = a.bm_num != nullptr;
   int n_qt = 0, t_first = 0;
   if (use_bm) {
     const int bb = (a.bm_batch == 1) ? 0 : b;
     const size_t bcol = (size_t)bb * a.bm_nkb + kt;
-    const int n_blocks = min(max(a.bm_qnum[bcol], 0), min(a.bm_nqb, kListCap));
+    int n_blocks = __builtin_amdgcn_readfirstlane(n_ranked);
+    if (n_blocks < 0) n_blocks = min(max(a.bm_qnum[bcol], 0), min(a.bm_nqb, kListCap));
     n_qt = 4 * n_blocks;
-    for (int t = tid; t < n_blocks; t += kThreads) {
-      s_qblk[t] = a.bm_qidx[bcol * a.bm_nqb + t];
-      s_qfull[t] = a.bm_qfull ? a.bm_qfull[bcol * a.bm_nqb + t] : 0;
-    }
+    stage_list_row<kListCap, kThreads>(a.bm_qidx + bcol * a.bm_nqb,
+                                       a.bm_qfull ? a.bm_qfull + bcol * a.bm_nqb : nullptr, n_blocks, s_qblk,
+                                       s_qfull, tid);
     __syncthreads();
   } else {
     int lo = 0, hi = a.Sq - 1;
@@ -532,6 +530,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     t_first = lo / kQTile;
     n_qt = (hi >= lo) ? hi / kQTile + 1 - t_first : 0;
   }
+#pragma unroll
+  for (int t = 0; t < VPL; ++t) {
+    const int idx = 64 * t + lane;
+    *(bf16x8 *)(v_rows[wave] + (idx / CPR) * VROW + 16 * (idx % CPR)) = vx[t];
+  }
+  const char *vrow = v_rows[wave] + l32 * VROW + 16 * h;
+  const float c_log2 = a.scale_log2;
+  const float cap2 = (MOD == kModCap) ? a.score.softcap * kLog2e : 0.0f;
+  const float cap_k = (MOD == kModCap) ? (2.0f / a.score.softcap) * c_log2 : 0.0f;
+  const float inv_cap2 = (MOD == kModCap) ? 1.0f / cap2 : 0.0f;
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
   const int n_iter = n_qt * G;   // (query head, query tile) pairs
 
   // Loads of a (head, tile) pair: Q and dO rows into LDS by buffer_load ...

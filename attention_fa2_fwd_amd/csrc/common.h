@@ -170,6 +170,38 @@ __device__ inline int work_ordered_tile(const int32_t *cnt, int n, int cap, int 
   return sel;
 }
 
+// Stages entries [0, n) of a BlockMask list row and their flags (flags may
+// be null: all 0) into LDS for a workgroup of NT threads, n <= CAP.  Every
+// load (range-checked buffer loads: a slot past n reads 0) is issued before
+// the first store, so the row costs one memory latency, shared with any
+// loads the caller issued before; the caller's barrier publishes the row.
+template <int CAP, int NT>
+__device__ inline void stage_list_row(const int32_t *idx, const uint8_t *flags, int n, int32_t *s_idx,
+                                      uint8_t *s_flag, int tid) {
+  const __amdgpu_buffer_rsrc_t l_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)idx, (short)0, n * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t f_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(flags ? (const void *)flags : (const void *)idx), (short)0, flags ? n : 0, 0x00020000);
+  constexpr int PER = CAP / NT;
+  int32_t v[PER];
+  uint8_t f[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    if (u * NT < n) {   // workgroup-uniform
+      v[u] = __builtin_amdgcn_raw_buffer_load_b32(l_rsrc, (tid + u * NT) * 4, 0, 0);
+      f[u] = __builtin_amdgcn_raw_buffer_load_b8(f_rsrc, tid + u * NT, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int t = tid + u * NT;
+    if (t < n) {
+      s_idx[t] = v[u];
+      s_flag[t] = f[u];
+    }
+  }
+}
+
 // Minimum / maximum of an int over the 64 lanes of a wave, in every lane, by
 // DPP (no LDS traffic): shifts by 1, 2, 4, 8 within each 16-lane row leave
 // the row's result in its lane 15; row_bcast:15 and row_bcast:31 carry it on

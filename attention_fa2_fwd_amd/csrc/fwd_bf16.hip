@@ -242,33 +242,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(KernelArgs a) {
     n_tiles = n_blocks * C::TPB;
     bm_list = a.bm_idx + row * a.bm_nkb;
     if (a.bm_full) bm_flags = a.bm_full + row * a.bm_nkb;
-    // Every load of the row (entries and flags, through range-checked
-    // buffer loads, so entries past n_blocks read as 0) is issued before the
-    // first store: one memory latency, shared with the Q and document-id
+    // The row's loads share one memory latency with the Q and document-id
     // loads issued above.
-    const __amdgpu_buffer_rsrc_t l_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void *)bm_list, (short)0, n_blocks * 4, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t f_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(bm_flags ? (const void *)bm_flags : (const void *)bm_list), (short)0, bm_flags ? n_blocks : 0,
-        kBufferFlags);
-    constexpr int kPer = kListCap / kThreads;
-    int32_t blk[kPer];
-    uint8_t full[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      if (u * kThreads < n_blocks) {   // wave-uniform
-        blk[u] = __builtin_amdgcn_raw_buffer_load_b32(l_rsrc, (tid + u * kThreads) * 4, 0, 0);
-        full[u] = __builtin_amdgcn_raw_buffer_load_b8(f_rsrc, tid + u * kThreads, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int t = tid + u * kThreads;
-      if (t < n_blocks) {
-        s_blk[t] = blk[u];
-        s_full[t] = full[u];
-      }
-    }
+    stage_list_row<kListCap, kThreads>(bm_list, bm_flags, n_blocks, s_blk, s_full, tid);
     __syncthreads();   // the list is read by every wave from here on
   } else {
     int lo = 0, hi = a.Skv;

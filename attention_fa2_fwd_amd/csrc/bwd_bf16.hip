@@ -156,8 +156,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __align__(16) char k_lds1[T::BYTES];
   __shared__ __align__(16) char v_lds0[T::BYTES];
   __shared__ __align__(16) char v_lds1[T::BYTES];
-  __shared__ __align__(16) int32_t kdoc0[kKTile];
-  __shared__ __align__(16) int32_t kdoc1[kKTile];
+  // Document ids of a staged key tile, then their min and max.
+  __shared__ __align__(16) int32_t kdoc0[kKTile + 4];
+  __shared__ __align__(16) int32_t kdoc1[kKTile + 4];
   __shared__ __align__(16) int32_t s_blk[kListCap];
   __shared__ uint8_t s_full[kListCap];
 
@@ -259,6 +260,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     }
     dsum = part + __shfl_xor(part, 32);
   }
+  // Range of the wave's document ids (rows past Sq repeat row Sq - 1).
+  const int dmin_w = DOC ? wave_min_i32(doc_i) : 0;
+  const int dmax_w = DOC ? wave_max_i32(doc_i) : 0;
+  // Wave 0 stages a key tile's ids (one per lane) with their min and max.
+  auto store_kdoc = [&](int32_t *dst, int id) __attribute__((always_inline)) {
+    dst[lane] = id;
+    const int mn = wave_min_i32(id), mx = wave_max_i32(id);
+    if (lane == 0) {
+      dst[kKTile] = mn;
+      dst[kKTile + 1] = mx;
+    }
+  };
   if (h == 0 && qi < a.Sq) a.row_dot[row] = dsum;
   const float c_log2 = a.scale_log2;
   const float bias2 = (MOD == kModAdd) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
@@ -310,7 +323,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   auto tile_step = [&](int k0, bool flag, const char *kt, const char *vt, const int32_t *kdoc)
       __attribute__((always_inline)) {
     if (block_empty<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1) || qw0 >= a.Sq || k0 >= a.Skv) return;
-    const bool full = (flag || block_full<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1)) && (k0 + kKTile <= a.Skv);
+    // Document masks: a tile whose id range misses the wave's holds no
+    // visible pair; one whose ids and the wave's are all one id is visible
+    // wherever the position part allows (no id test per element).
+    bool one_id = false;
+    if (DOC) {
+      const int kmn = kdoc[kKTile], kmx = kdoc[kKTile + 1];
+      if (kmx < dmin_w || kmn > dmax_w) return;
+      one_id = (kmn == kmx) && (dmin_w == dmax_w) && (kmn == dmin_w);
+    }
+    const bool pos_full = (MASK == ATTN_MASK_DOCUMENT) ? (k0 + kKTile - 1 <= qw0)
+                        : (MASK == kMaskDocWindow) ? ((k0 + kKTile - 1 <= qw0) && (qw1 - k0 < a.mask.window))
+                        : false;
+    const bool full = (flag || block_full<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1) || (one_id && pos_full)) &&
+                      (k0 + kKTile <= a.Skv);
     // S^T and dP^T for the two 32-key blocks.
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -373,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   if (n_tiles > 0) {
     load_tile(k_lds0, k_rsrc, tile_key0(0));
     load_tile(v_lds0, v_rsrc, tile_key0(0));
-    if (DOC && wave == 0) kdoc0[lane] = load_doc(tile_key0(0));
+    if (DOC && wave == 0) store_kdoc(kdoc0, load_doc(tile_key0(0)));
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
@@ -395,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       if (DOC && wave == 0) doc_fill = load_doc(k1);
     }
     if (n < n_tiles) tile_step(k0, f0, k_cur, v_cur, d_cur);
-    if (DOC && wave == 0 && n + 1 < n_tiles) d_nxt[lane] = doc_fill;
+    if (DOC && wave == 0 && n + 1 < n_tiles) store_kdoc(d_nxt, doc_fill);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };

@@ -12,9 +12,12 @@
 //
 // Layout of the work (CDNA4-specific choices):
 //  * workgroup = 256 threads = 4 wave64s, 128 query rows; each wave owns 32
-//    consecutive rows.  Key tiles of 64 rows (128 for unmasked D=64).  Two
-//    workgroups per CU, so each SIMD interleaves two waves: one's MFMAs run
-//    beside the other's softmax.
+//    consecutive rows.  With grouped heads (Hq / Hkv a multiple of 4, no
+//    BlockMask) the 128 rows are 32 positions of four heads sharing a kv
+//    head, one head per wave, so all four waves need the same key tiles.
+//    Key tiles of 64 rows (128 for unmasked D=64).  Two workgroups per CU,
+//    so each SIMD interleaves two waves: one's MFMAs run beside the other's
+//    softmax.
 //  * Scores are computed transposed, S^T = K·Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand, Q^T (kept in
 //    VGPRs for the whole kernel) the B operand.  In the 32x32 accumulator
@@ -51,9 +54,12 @@
 //    index is permuted so that each XCD works on a contiguous run of heads,
 //    and the query heads of a GQA group read their K/V through one L2.
 //  * Causal-type masks: workgroups with the most key tiles are launched
-//    first (with a BlockMask, the query tiles with the most listed blocks);
-//    waves skip tiles that hold no visible key for their rows and skip the
-//    predicate on tiles where every key is visible.
+//    first (with a BlockMask, the query tiles with the most listed blocks,
+//    ranked by each wave in registers); waves skip tiles that hold no
+//    visible key for their rows and skip the predicate on tiles where every
+//    key is visible.
+//  * The bf16 output leaves through LDS: each wave stages its rows in a
+//    free tile buffer and stores whole rows, 16 bytes per lane.
 #include <type_traits>
 
 #include "kernels.h"

@@ -259,7 +259,10 @@ size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int D, int max_pag
  *   never read, and what the slots of earlier keys hold (NaN included) has
  *   no effect.  ALIBI / REL_POS use i = seq_lens[s] - 1.
  *   workspace: device scratch of at least
- *   attn_paged_decode_workspace_size(...) bytes, 256-byte aligned.
+ *   attn_paged_decode_workspace_size(...) bytes, 256-byte aligned.  When
+ *   every key range fits 128 pages (max_pages_per_seq, or the window, small
+ *   enough) and N * Hkv >= 256, each sequence is one work item written
+ *   straight to out / lse and the workspace is not touched.
  * Supported: dt = BF16, D == 128, page_size == 16, Hq % Hkv == 0,
  * Hq / Hkv <= 16, mk in {NONE, SLIDING} (others return -2).               */
 int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
@@ -281,7 +284,8 @@ int attn_paged_decode(const void *q, const void *k_cache, const void *v_cache,
  *   Scratch needed: N * Hq * splits * (D + 1) * 4 bytes (plus padding),
  *   with splits = the key splits per sequence this launch takes (64 pages
  *   each, or 32 / 16 when that leaves too few work items), bounded by
- *   max_pages_per_seq and the window.  A request needing more returns -4
+ *   max_pages_per_seq and the window; 0 when each sequence is one work item
+ *   written straight to the output (as attn_paged_decode).  A request needing more returns -4
  *   (ATTN_ERR_WORKSPACE) with the sizes in attn_last_error(); the 64-sequence,
  *   32-head, 2048-page shape needs 33.8 MB.
  *   Every call on one GPU shares that GPU's scratch: calls that may overlap

@@ -209,11 +209,12 @@ def test_paged_decode_sliding_window(window):
     run_decode(small_decode_inputs(LENGTHS, seed=5), "alibi", "window", window=window)
 
 
-@pytest.mark.parametrize("n_seq,window,split", [(64, 0, 64), (40, 0, 32), (40, 700, 16)])
+@pytest.mark.parametrize("n_seq,window,split", [(64, 0, 64), (40, 0, 32), (20, 700, 16)])
 def test_paged_decode_split_sizes(n_seq, window, split):
     # The launch takes 64-, 32- or 16-page splits depending on how many work
     # items the sequence count, the kv heads and the longest key range give
-    # (2048 wanted); these shapes land on each size in turn.
+    # (2048 wanted); these shapes land on each size in turn (20 sequences x 8
+    # kv heads are too few items for the one-item-per-sequence form).
     rng = np.random.default_rng(n_seq + window)
     lengths = rng.integers(1, 300 * 16 + 1, size=n_seq)
     lengths[:3] = [0, 1, 300 * 16]
@@ -238,8 +239,10 @@ def test_paged_decode_window_skips_pages_before_it():
 
 
 def test_paged_decode_many_sequences_and_empty_ones():
-    # More sequences than one 64-wide chunk of the work enumeration, lengths
-    # that give 0, 1 and 2 splits, and empty sequences (O = 0, LSE = -inf).
+    # More sequences than one 64-wide chunk of the work enumeration and empty
+    # sequences (O = 0, LSE = -inf).  150 sequences x 2 kv heads over at most
+    # 80 pages run as one item per (sequence, kv head), written straight to
+    # the output.
     rng = np.random.default_rng(11)
     lengths = [int(x) for x in rng.integers(0, 200, size=150)]
     lengths[0] = 0
@@ -249,6 +252,18 @@ def test_paged_decode_many_sequences_and_empty_ones():
     lengths[100] = 1024
     inp = small_decode_inputs(lengths, hq=8, hkv=2, seed=4)
     run_decode(inp, "alibi", "many sequences")
+
+
+# One work item per (sequence, kv head), reduced straight into the output,
+# when every key range fits 128 pages and there are at least 256 items: 33
+# sequences x 8 kv heads, lengths from 0 to 3000, NaN in every slot no
+# sequence owns.  Window 2032 is the largest whose range fits 128 pages;
+# 2033 takes the split path with the same inputs.
+@pytest.mark.parametrize("window", [1, 16, 100, 1024, 2032, 2033])
+def test_paged_decode_direct_items(window):
+    lengths = [0, 1, 15, 16, 17, 1023, 1024, 1025, 2040, 3000] + [37 * k + 5 for k in range(23)]
+    inp = small_decode_inputs(lengths, hq=32, hkv=8, max_pages=200, seed=window, poison=True)
+    run_decode(inp, "alibi", "direct items", window=window)
 
 
 def test_paged_decode_full_workload_sampled():

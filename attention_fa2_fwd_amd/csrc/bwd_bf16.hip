@@ -85,6 +85,7 @@ struct BwdArgs {
   const int32_t *bm_num, *bm_idx, *bm_qnum, *bm_qidx;
   const uint8_t *bm_full, *bm_qfull;
   int bm_nqb, bm_nkb, bm_batch;
+  int gqa_pack;   // 1: a dQ workgroup is 32 positions of four query heads sharing a kv head
 };
 
 __device__ __forceinline__ s16x4 lds_read_tr(const char *p) {
@@ -168,14 +169,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const int n_qtiles = (a.Sq + kQRows - 1) / kQRows;
-  const int bh_count = a.B * a.Hq;
+  // Rows of the workgroup: 128 consecutive rows of one head, wave w taking
+  // rows 32w .. 32w + 31; or, with gqa_pack (Hq / Hkv a multiple of 4, no
+  // BlockMask), 32 positions of four heads sharing a kv head, wave w taking
+  // head 4g + w, so every wave needs the same key tiles.
+  const int pack = a.gqa_pack;
+  const int rows = pack ? 32 : kQRows;
+  const int n_qtiles = (a.Sq + rows - 1) / rows;
+  const int hunits = pack ? a.Hq / 4 : a.Hq;
+  const int bh_count = a.B * hunits;
   // Workgroups go round-robin to the 8 XCDs; each XCD gets a contiguous run
-  // of heads, so the query heads of one kv head share an L2.
+  // of head units, so the query heads of one kv head share an L2.
   const int xh = (int)(blockIdx.x % bh_count);
   const int bh = (bh_count % 8 == 0) ? (xh % 8) * (bh_count / 8) + xh / 8 : xh;
-  const int b = bh / a.Hq;
-  const int hq = bh - b * a.Hq;
+  const int b = bh / hunits;
+  const int hu = bh - b * hunits;
+  const int hq = pack ? 4 * hu + __builtin_amdgcn_readfirstlane(tid >> 6) : hu;
   // Longest key ranges first: the later query tiles, or with a BlockMask the
   // tiles with the most listed blocks (each wave ranks the counts itself).
   const int pos = (int)(blockIdx.x / bh_count);
@@ -187,8 +196,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
                            &n_ranked);
   }
   const int hkv = (hq * a.Hkv) / a.Hq;
-  const int q0 = qt * kQRows;
-  const int qw0 = q0 + wave * 32;
+  const int q0 = qt * rows;
+  const int qw0 = pack ? q0 : q0 + wave * 32;
   const int qw1 = min(qw0 + 31, a.Sq - 1);
   const int qi = qw0 + l32;
   const int qr = min(qi, a.Sq - 1);
@@ -234,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
                                        s_full, tid);
     __syncthreads();
   } else {
-    const int qlast = min(q0 + kQRows, a.Sq) - 1;
+    const int qlast = min(q0 + rows, a.Sq) - 1;
     int lo = 0, hi = a.Skv;
     if (MASK == ATTN_MASK_CAUSAL || MASK == ATTN_MASK_DOCUMENT) {
       hi = min(a.Skv, qlast + 1);
@@ -785,7 +794,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
 template <int D, int MASK, int MOD>
 hipError_t launch_main(const BwdArgs &a, hipStream_t stream) {
-  const unsigned grid_q = (unsigned)(((a.Sq + kQRows - 1) / kQRows) * a.B * a.Hq);
+  const int rows_q = a.gqa_pack ? 32 : kQRows;
+  const unsigned grid_q = (unsigned)(((a.Sq + rows_q - 1) / rows_q) * a.B * (a.gqa_pack ? a.Hq / 4 : a.Hq));
   if (grid_q > 0) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD>), dim3(grid_q), dim3(kThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
@@ -843,6 +853,9 @@ hipError_t launch_d(const BwdParams &p, hipStream_t stream) {
   a.bm_nqb = p.bm_nqb;
   a.bm_nkb = p.bm_nkb;
   a.bm_batch = p.bm_batch;
+  // dQ: grouped heads in fours when the analytic key range applies (a
+  // BlockMask row covers 128 query rows).
+  a.gqa_pack = (p.bm_num == nullptr && p.Hkv > 0 && (p.Hq / p.Hkv) % 4 == 0) ? 1 : 0;
   if (p.score.kind == ATTN_SCORE_SOFTCAP) return launch_mask<D, kModCap>(a, stream);
   if (p.score.kind == ATTN_SCORE_NONE) return launch_mask<D, kModRaw>(a, stream);
   return launch_mask<D, kModAdd>(a, stream);

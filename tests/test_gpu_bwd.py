@@ -145,6 +145,34 @@ def test_bwd_gqa_groups(G):
     run_bwd(1, 2 * G, 2, 260, 260, 64, "causal", "none", seed=G)
 
 
+# Groups of four or more query heads per kv head run the dQ pass as
+# workgroups of 32 positions x 4 heads (no BlockMask): against the oracle,
+# and dQ bit for bit against the same call with K/V expanded to every query
+# head (dK / dV sum the group's heads, so they are held to the oracle only).
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", MASKS)
+def test_bwd_gqa_four_head_dq_workgroups(D, mask):
+    B, Hq, Hkv, S = 1, 8, 2, 300
+    run_bwd(B, Hq, Hkv, S, S, D, mask, "alibi", seed=D + len(mask), window=77)
+    q, k, v = workloads.randn_qkv(B, Hq, Hkv, S, S, D, "bf16", D + len(mask))
+    do = workloads.randn_qkv(B, Hq, Hkv, S, S, D, "bf16", D + len(mask) + 1000)[0]
+    dev = torch.device("cuda")
+    dd = None
+    if has_document(mask):
+        lens = [50, 130, 7, 113]
+        lens[-1] += S - sum(lens)
+        dd = torch.from_numpy(workloads.doc_ids_from_lengths(lens, B)).to(dev)
+    kw = dict(mask=mask, window=77, prefix_len=70, doc_ids=dd, score="alibi")
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    out, lse = af.attn_fwd(qd, kd, vd, **kw)
+    dq, _, _ = af.attn_bwd(qd, kd, vd, out, lse, dod, **kw)
+    kr = kd.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+    vr = vd.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+    dq_m, _, _ = af.attn_bwd(qd, kr, vr, out, lse, dod, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq_m)
+
+
 def test_bwd_deterministic():
     dev = torch.device("cuda")
     q, k, v = (t.to(dev) for t in workloads.randn_qkv(1, 8, 2, 700, 700, 128, "bf16", 3))

@@ -19,8 +19,10 @@
 // (v_mfma_f32_32x32x16_bf16, 4 waves x 32 rows, LDS tiles of 1 KiB row
 // blocks filled by buffer_load ... lds and read either row-wise or through
 // the transposing ds_read_b64_tr_b16):
-//  * bwd_dq_kernel, one workgroup per (b, hq, 128 query rows), streams 64-key
-//    tiles of K and V.  S^T = K Q^T and dP^T = V dO^T take K and V rows from
+//  * bwd_dq_kernel, one workgroup per (b, hq, 128 query rows) (with groups
+//    of four or more query heads and no BlockMask, per 32 positions of four
+//    heads sharing a kv head, one head per wave), streams 64-key tiles of K
+//    and V.  S^T = K Q^T and dP^T = V dO^T take K and V rows from
 //    LDS as the A operand and Q^T, dO^T from registers as the B operand; the
 //    lane then holds one query and 16 keys, so LSE and D are one register
 //    each, and dS^T leaves the accumulator already in the B-operand layout of
@@ -37,7 +39,8 @@
 // Tiles without a visible pair are skipped and the predicate is dropped on
 // tiles where every pair is visible, from the mask's closed-form bounds or,
 // given a BlockMask, from its lists: by query block for the dQ pass, by key
-// block for the dK/dV pass, staged in LDS.  The tiles with the most work
+// block for the dK/dV pass, staged in LDS.  Under document masks the dQ pass
+// also compares each key tile's document-id range with its wave's.  The tiles with the most work
 // launch first in both passes (with a BlockMask, ranked by list length).
 #include "kernels.h"
 

@@ -266,6 +266,15 @@ def test_paged_decode_direct_items(window):
     run_decode(inp, "alibi", "direct items", window=window)
 
 
+@pytest.mark.parametrize("score", ["none", "rel_pos", "softcap"])
+def test_paged_decode_direct_items_scores(score):
+    # the other score forms on the direct items (no window: 33 sequences of at
+    # most 120 pages, within one item each)
+    lengths = [0, 1, 16, 17, 1900] + [53 * k + 7 for k in range(28)]
+    inp = small_decode_inputs(lengths, hq=16, hkv=8, max_pages=120, seed=40 + len(score), poison=True)
+    run_decode(inp, score, "direct items, no window")
+
+
 def test_paged_decode_full_workload_sampled():
     w = workloads.PAGED_DECODE
     dev = torch.device("cuda")

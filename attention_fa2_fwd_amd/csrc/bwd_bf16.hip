@@ -50,7 +50,6 @@ namespace {
 constexpr int kThreads = 256;
 // Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kBufferFlags = 0x00020000;
-constexpr int kPad = 64;           // bytes between LDS row blocks
 constexpr int kQRows = 128;        // query rows per dQ workgroup
 constexpr int kKTile = 64;         // key rows per tile in the dQ kernel
 constexpr int kKRows = 128;        // keys per dK/dV workgroup
@@ -61,19 +60,103 @@ constexpr int kModAdd = 0, kModCap = 1, kModRaw = 2;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS tile of ROWS rows of D bf16: row t lives in 1 KiB block t % NB at slot
-// t / NB, blocks padded apart.
+// LDS tile of ROWS rows of D bf16.  The LDS DMA fills it in 1 KiB blocks
+// (load i of wave w fills block 4i + w, its lane L bytes 16L .. 16L + 15),
+// and it is read two ways: 16-byte row reads, whose 16-lane passes read 16
+// consecutive rows at one chunk, and transposing reads, whose 32-lane passes
+// read 64 bytes of each of 4 consecutive rows.  LDS has 64 banks of 4 bytes,
+// so a row-read pass is free of conflicts when its 16 rows put the chunk on
+// 16 distinct 16-byte bank slots, and a transposing pass when its 4 rows
+// start on slots 4 apart.  Rows are placed in blocks and slots, and the
+// 16-byte chunks of row q permuted as chunk ^ xr(q), so that both hold:
+//  - D = 128 (4 rows per block): row q = 16c + 8a + 4h + j sits in block
+//    2j + a (+ 8h in a 16-block tile) at slot c (2c + h in an 8-block
+//    tile), chunks XOR h; blocks 1056 bytes apart put block b on slot 2b.
+//  - D = 64 (8 rows per block): row q sits in block q % NB at slot q / NB,
+//    chunks XOR (q / 4) % 4; blocks 1088 bytes apart put block b on slot 4b.
+// In both, each lane's read addresses are one base per kind of read plus
+// compile-time steps, and the loads of a wave are one offset plus
+// compile-time changes; check() verifies this for every lane.
 template <int D, int ROWS>
 struct Tile {
   static constexpr int ROWB = D * 2;
-  static constexpr int NB = ROWS * ROWB / 1024;
-  static constexpr int BLK = 1024 + kPad;
+  static constexpr int NB = ROWS * ROWB / 1024;     // blocks
+  static constexpr int SPB = 1024 / ROWB;           // rows per block
+  static constexpr bool PERM = D == 128;
+  static constexpr int BLK = PERM ? 1024 + 32 : 1024 + 64;
   static constexpr int BYTES = NB * BLK;
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int LOADS = NB / 4;              // direct loads per wave per tile
+  static_assert(D == 64 || D == 128, "head dim");
   static_assert(NB % 4 == 0 && 32 % NB == 0 && (NB <= 8 || NB == 16), "row block mapping");
-  static constexpr int off(int t) { return (t % NB) * BLK + (t / NB) * ROWB; }
+  static_assert(!PERM || NB == 8 || NB == 16, "D = 128 placement");
+
+  static constexpr int blk(int q) {
+    return PERM ? 2 * (q & 3) + ((q >> 3) & 1) + (NB == 16 ? 8 * ((q >> 2) & 1) : 0) : q % NB;
+  }
+  static constexpr int slot(int q) { return PERM ? (NB == 16 ? q >> 4 : 2 * (q >> 4) + ((q >> 2) & 1)) : q / NB; }
+  static constexpr int xr(int q) { return PERM ? (q >> 2) & 1 : (q >> 2) & 3; }
+  static constexpr int row_off(int q) { return blk(q) * BLK + slot(q) * ROWB; }
+  static constexpr int row_at(int b, int s) {
+    if (!PERM) return b + NB * s;
+    const int h = NB == 16 ? b >> 3 : s & 1, c = NB == 16 ? s : s >> 1;
+    return 16 * c + 8 * (b & 1) + 4 * h + ((b >> 1) & 3);
+  }
+  // Source byte offset (from the tile's first row) of lane L's 16 bytes in
+  // load i of wave w; load i's equals (load 0's ^ 16 lxor(i)) + i RSTEP.
+  static constexpr int src(int w, int L, int i) {
+    const int q = row_at(4 * i + w, L / CPR);
+    return q * ROWB + 16 * ((L % CPR) ^ xr(q));
+  }
+  static constexpr int RSTEP = PERM ? 2 * ROWB : 4 * ROWB;
+  static constexpr int lxor(int i) { return PERM ? (NB == 16 ? i >> 1 : 0) : i; }
+  // Row reads: lane (h, l32) reads row l32 + 32 kb, chunk 2c + h at
+  // row_base(l32, h, c % 2) + row_step(kb) + 32c.
+  static constexpr int row_base_def(int l32, int h, int e) {
+    return row_off(l32) + 16 * ((2 * e + h) ^ xr(l32)) - 32 * e;
+  }
+  static constexpr int row_step(int kb) { return row_off(32 * kb) - row_off(0); }
+  // Transposing reads: within each 16-lane group, lanes 4r .. 4r + 3 point at
+  // 4 consecutive d of row 16c + 8 hi + 4h + r (d = 32 ((lane >> 4) & 1) +
+  // 4 (lane & 3) + 32 db), at tr_base(lane, hi) + tr_step(c, hi) + 64 db.
+  static constexpr int tr_base_def(int lane, int hi) {
+    const int tj = lane & 15, r = 8 * hi + 4 * (lane >> 5) + (tj >> 2);
+    return row_off(r) + 16 * ((2 * ((lane >> 4) & 1) + ((tj & 3) >> 1)) ^ xr(r)) + 8 * (tj & 1);
+  }
+  static constexpr int tr_step(int c, int hi) { return row_off(16 * c + 8 * hi) - row_off(8 * hi); }
+  // The D = 128 placement needs one base of each kind (the XOR flips only
+  // the chunk bit a lane's h gives; row 8 + r sits one block after row r);
+  // written so, the compiler keeps one register for each.
+  static constexpr int row_base(int l32, int h, int e) { return row_base_def(l32, h, PERM ? 0 : e); }
+  static constexpr int tr_base(int lane, int hi) { return PERM ? tr_base_def(lane, 0) + hi * BLK : tr_base_def(lane, hi); }
+
+  static constexpr bool check() {
+    bool seen[ROWS] = {};
+    for (int q = 0; q < ROWS; ++q) {
+      if (blk(q) >= NB || slot(q) >= SPB || row_at(blk(q), slot(q)) != q || seen[q]) return false;
+      seen[q] = true;
+    }
+    for (int w = 0; w < 4; ++w)
+      for (int L = 0; L < 64; ++L)
+        for (int i = 0; i < LOADS; ++i)
+          if (src(w, L, i) != ((src(w, L, 0) ^ (16 * lxor(i))) + i * RSTEP)) return false;
+    for (int kb = 0; kb < ROWS / 32; ++kb)
+      for (int l = 0; l < 32; ++l)
+        if (row_off(32 * kb + l) - row_off(l) != row_step(kb) || xr(32 * kb + l) != xr(l)) return false;
+    for (int c = 0; c < ROWS / 16; ++c)
+      for (int r = 0; r < 16; ++r)
+        if (row_off(16 * c + r) - row_off(r) != tr_step(c, r >> 3) || xr(16 * c + r) != xr(r)) return false;
+    for (int lane = 0; lane < 64; ++lane)
+      for (int e = 0; e < 2; ++e)
+        if (row_base(lane & 31, lane >> 5, e) != row_base_def(lane & 31, lane >> 5, e) ||
+            tr_base(lane, e) != tr_base_def(lane, e))
+          return false;
+    return true;
+  }
 };
+static_assert(Tile<64, 32>::check() && Tile<64, 64>::check() && Tile<128, 32>::check() &&
+                  Tile<128, 64>::check(),
+              "LDS tile placement");
 
 struct BwdArgs {
   const __bf16 *q, *k, *v, *out, *dout;
@@ -311,26 +394,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       (void *)(a.v + kv_base), (short)0, a.Skv * D * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t d_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(doc_row ? doc_row : a.mask.doc_ids), (short)0, doc_row ? a.Skv * 4 : 0, kBufferFlags);
-  // Load i of wave w fills row block 4i + w: lane L writes its 16 bytes at
-  // slot L / CPR, chunk L % CPR (row (4i + w) + NB * (L / CPR)).
-  const int ld_off = ((wave + T::NB * (lane / T::CPR)) * D + (lane % T::CPR) * 8) * 2;
+  const int ld_off = T::src(wave, lane, 0);
   auto load_tile = [&](char *dst, __amdgpu_buffer_rsrc_t rs, int row0) __attribute__((always_inline)) {
     const int soff = __builtin_amdgcn_readfirstlane(row0 * D * 2);
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (4 * i + wave) * T::BLK), 16,
-                                               ld_off + i * (4 * D * 2), soff, 0, 0);
+    for (int i = 0; i < T::LOADS; ++i) {
+      // (A type-dependent expression among this builtin's arguments makes
+      // the host pass drop the kernel's launch stub: offsets are computed
+      // first.)
+      const int vo = (ld_off ^ (16 * T::lxor(i))) + i * T::RSTEP;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (4 * i + wave) * T::BLK), 16, vo, soff, 0, 0);
+    }
   };
   auto load_doc = [&](int key0) __attribute__((always_inline)) -> int {
     return __builtin_amdgcn_raw_buffer_load_b32(d_rsrc, lane * 4, __builtin_amdgcn_readfirstlane(key0 * 4), 0);
   };
 
-  // Row reads (A operand, rows 32 kb + l32, d chunk 16c + 8h) and transposed
-  // reads (A operand K^T: lane groups of 4 point at 4 consecutive d of key
-  // 4h + (lane & 15) / 4 of each 8-key half chunk).
-  const int rd_row = T::off(l32) + h * 16;
-  const int tr_j = lane & 15;
-  const int rd_tr = T::off(4 * h + (tr_j >> 2)) + (16 * ((lane >> 4) & 1) + 4 * (tr_j & 3)) * 2;
+  // Row reads (A operand, keys 32 kb + l32, d chunk 2c + h) and transposed
+  // reads (A operand K^T: the first and second 8 keys of each 16-key chunk).
+  const int rd_row0 = T::row_base(l32, h, 0), rd_row1 = T::row_base(l32, h, 1);
+  const int rd_tr0 = T::tr_base(lane, 0), rd_tr1 = T::tr_base(lane, 1);
 
   auto tile_step = [&](int k0, bool flag, const char *kt, const char *vt, const int32_t *kdoc)
       __attribute__((always_inline)) {
@@ -357,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       dp[kb] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
-        const int o = rd_row + T::off(32 * kb) + 32 * c;
+        const int o = ((c & 1) ? rd_row1 : rd_row0) + T::row_step(kb) + 32 * c;
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(kt + o), qf[c], s[kb], 0, 0, 0);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(vt + o), df[c], dp[kb], 0, 0, 0);
       }
@@ -384,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     // wave feeding the matrix cores issues ahead of the other wave's
     // elementwise work (measured 6-9% faster on the causal D=64 backward).
     __builtin_amdgcn_s_setprio(1);
-    const char *kbase = kt + rd_tr;
+    const char *kbase0 = kt + rd_tr0, *kbase1 = kt + rd_tr1;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       asm volatile("" ::: "memory");   // keep this chunk's LDS reads in the chunk
@@ -395,8 +478,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const s16x4 lo4 = lds_read_tr(kbase + T::off(16 * c) + 64 * db);
-        const s16x4 hi4 = lds_read_tr(kbase + T::off(16 * c + 8) + 64 * db);
+        const s16x4 lo4 = lds_read_tr(kbase0 + T::tr_step(c, 0) + 64 * db);
+        const s16x4 hi4 = lds_read_tr(kbase1 + T::tr_step(c, 1) + 64 * db);
         const u32x4 kw = {__builtin_bit_cast(u32x2, lo4)[0], __builtin_bit_cast(u32x2, lo4)[1],
                           __builtin_bit_cast(u32x2, hi4)[0], __builtin_bit_cast(u32x2, hi4)[1]};
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kw), pb, acc[db], 0, 0, 0);
@@ -590,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
   // Loads of a (head, tile) pair: Q and dO rows into LDS by buffer_load ...
   // lds (rows past Sq read as zero), the per-query values by wave 0.
-  const int ld_off = ((wave + T::NB * (lane / T::CPR)) * D + (lane % T::CPR) * 8) * 2;
+  const int ld_off = T::src(wave, lane, 0);
   // A step is one (query head, query tile) pair, heads outer; steps advance
   // one at a time, so finding a step's head and tile needs no division.
   struct Step {
@@ -620,10 +703,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const int soff = __builtin_amdgcn_readfirstlane(q0 * D * 2);
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)(qd + (4 * i + wave) * T::BLK), 16,
-                                               ld_off + i * (4 * D * 2), soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(orr, (lds_void *)(od + (4 * i + wave) * T::BLK), 16,
-                                               ld_off + i * (4 * D * 2), soff, 0, 0);
+      const int vo = (ld_off ^ (16 * T::lxor(i))) + i * T::RSTEP;   // (see the dQ kernel's loads)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)(qd + (4 * i + wave) * T::BLK), 16, vo, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(orr, (lds_void *)(od + (4 * i + wave) * T::BLK), 16, vo, soff, 0, 0);
     }
   };
   // Per-query values for lane < 32 of wave 0: LSE in log2 units (+inf past
@@ -651,9 +733,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  const int rd_row = T::off(l32) + h * 16;
-  const int tr_j = lane & 15;
-  const int rd_tr = T::off(4 * h + (tr_j >> 2)) + (16 * ((lane >> 4) & 1) + 4 * (tr_j & 3)) * 2;
+  const int rd_row0 = T::row_base(l32, h, 0), rd_row1 = T::row_base(l32, h, 1);
+  const int rd_tr0 = T::tr_base(lane, 0), rd_tr1 = T::tr_base(lane, 1);
 
   auto tile_step = [&](Step st, int i0, bool flag, const char *qt_, const char *ot, const float *ls,
                        const float *dt,
@@ -668,7 +749,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
-      const int o = rd_row + 32 * c;
+      const int o = ((c & 1) ? rd_row1 : rd_row0) + 32 * c;
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(qt_ + o), kf[c], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(ot + o),
                                                    *(const bf16x8 *)(vrow + 32 * c), dp, 0, 0, 0);
@@ -710,8 +791,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       sw[2 * g + 1] = pack_bf16x2(dr[2], dr[3]);
     }
     // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time.
-    const char *obase = ot + rd_tr;
-    const char *qbase = qt_ + rd_tr;
+    const char *obase0 = ot + rd_tr0, *obase1 = ot + rd_tr1;
+    const char *qbase0 = qt_ + rd_tr0, *qbase1 = qt_ + rd_tr1;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]});
@@ -719,13 +800,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       asm volatile("" ::: "memory");   // keep this chunk's LDS reads in the chunk
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const s16x4 olo = lds_read_tr(obase + T::off(16 * c) + 64 * db);
-        const s16x4 ohi = lds_read_tr(obase + T::off(16 * c + 8) + 64 * db);
+        const s16x4 olo = lds_read_tr(obase0 + T::tr_step(c, 0) + 64 * db);
+        const s16x4 ohi = lds_read_tr(obase1 + T::tr_step(c, 1) + 64 * db);
         const u32x4 ow = {__builtin_bit_cast(u32x2, olo)[0], __builtin_bit_cast(u32x2, olo)[1],
                           __builtin_bit_cast(u32x2, ohi)[0], __builtin_bit_cast(u32x2, ohi)[1]};
         dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ow), pb, dv[db], 0, 0, 0);
-        const s16x4 qlo = lds_read_tr(qbase + T::off(16 * c) + 64 * db);
-        const s16x4 qhi = lds_read_tr(qbase + T::off(16 * c + 8) + 64 * db);
+        const s16x4 qlo = lds_read_tr(qbase0 + T::tr_step(c, 0) + 64 * db);
+        const s16x4 qhi = lds_read_tr(qbase1 + T::tr_step(c, 1) + 64 * db);
         const u32x4 qw = {__builtin_bit_cast(u32x2, qlo)[0], __builtin_bit_cast(u32x2, qlo)[1],
                           __builtin_bit_cast(u32x2, qhi)[0], __builtin_bit_cast(u32x2, qhi)[1]};
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qw), sb, dk[db], 0, 0, 0);

@@ -708,10 +708,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(orr, (lds_void *)(od + (4 * i + wave) * T::BLK), 16, vo, soff, 0, 0);
     }
   };
-  // Per-query values for lane < 32 of wave 0: LSE in log2 units (+inf past
-  // Sq, so p = 0 there), D, document id.
+  // Per-query values for lane < 32 of wave 0: LSE (+inf past Sq, so p = 0
+  // there), D, document id.  The LSE goes to log2 units only when it is
+  // stored, after the step's work: converting it where it is fetched makes
+  // the wave wait there for its load, and with it for the next tiles' loads.
+  // (An empty asm keeps the compiler from moving the product back up.)
   struct QVals {
-    float lse2, dot;
+    float lse, dot;
     int doc;
   };
   auto fetch_qvals = [&](Step st, int q0) __attribute__((always_inline)) -> QVals {
@@ -719,7 +722,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     QVals r{INFINITY, 0.0f, -1};
     if (lane < kQTile && i < a.Sq) {
       const size_t row = (size_t)(b * a.Hq + st.hq) * a.Sq + i;
-      r.lse2 = a.lse[row] * kLog2e;
+      r.lse = a.lse[row];
       r.dot = a.row_dot[row];
       if (DOC) r.doc = doc_row[i];
     }
@@ -727,7 +730,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   };
   auto store_qvals = [&](const QVals &r, float *ls, float *dt, int32_t *dc) __attribute__((always_inline)) {
     if (lane < kQTile) {
-      ls[lane] = r.lse2;
+      float lse = r.lse;
+      asm volatile("" : "+v"(lse));
+      ls[lane] = lse * kLog2e;
       dt[lane] = r.dot;
       if (DOC) dc[lane] = r.doc;
     }

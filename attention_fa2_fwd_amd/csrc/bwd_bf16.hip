@@ -210,6 +210,17 @@ __device__ __forceinline__ bool block_full(const MaskArgs &m, int i0, int i1, in
   return false;
 }
 
+// Bias coefficient of query head hq (wave-uniform) with a slope table read
+// through the scalar cache: a wait for it then never waits for the vector
+// loads in flight.
+__device__ __forceinline__ float bias_coeff_uniform(const ScoreArgs &s, int hq, int Hq) {
+  if (s.kind == ATTN_SCORE_ALIBI && s.slopes) {
+    typedef __attribute__((address_space(4))) const float *const_f32p;
+    return ((const_f32p)s.slopes)[__builtin_amdgcn_readfirstlane(hq)];
+  }
+  return bias_coeff(s, hq, Hq);
+}
+
 // Log2-domain modified score of raw dot product s, and the factor
 // score_mod'(x) of the chain rule.  With a bias, bias2 (j - i) is passed as
 // base + bias2 * off: base per tile and lane, off a compile-time offset of
@@ -741,14 +752,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int rd_row0 = T::row_base(l32, h, 0), rd_row1 = T::row_base(l32, h, 1);
   const int rd_tr0 = T::tr_base(lane, 0), rd_tr1 = T::tr_base(lane, 1);
 
-  auto tile_step = [&](Step st, int i0, bool flag, const char *qt_, const char *ot, const float *ls,
+  auto tile_step = [&](int i0, bool flag, float bias2, const char *qt_, const char *ot, const float *ls,
                        const float *dt,
                        const int32_t *dc) __attribute__((always_inline)) {
     const int i1 = i0 + kQTile - 1;
     if (jw0 >= a.Skv || i0 >= a.Sq || block_empty<MASK>(a.mask, i0, i1, jw0, jw1)) return;
     const bool full = flag || block_full<MASK>(a.mask, i0, i1, jw0, jw1);
-    const int hq = st.hq;
-    const float bias2 = (MOD == kModAdd) ? bias_coeff(a.score, hq, a.Hq) * kLog2e : 0.0f;
     // S = Q K^T and dP = dO V^T for the 32 queries: element r is query
     // i0 + 8 (r / 4) + 4h + r % 4, key kj.
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -830,6 +839,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // iteration that loaded it, so an iteration looks up one list entry.
   int q0_cur = (n_iter > 0) ? __builtin_amdgcn_readfirstlane(tile_q0(first.t)) : 0;
   bool flag_cur = (n_iter > 0) && tile_flag(first.t);
+  // The bias coefficient of the step's query head is carried the same way:
+  // taken where it is needed, its optional table load made the wave wait
+  // there for the next tiles' loads as well.  The empty asm keeps the log2
+  // scaling at the use.
+  float bias_cur = (MOD == kModAdd) ? bias_coeff_uniform(a.score, first.hq, a.Hq) : 0.0f;
   // Iteration it (step st): load step it + 1 into the buffers step it - 1
   // used, compute step it, wait for this wave's loads, barrier.
   auto iteration = [&](int it, Step st, char *q_cur, char *o_cur, float *l_cur, float *d_cur,
@@ -837,6 +851,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
                        int32_t *c_nxt) __attribute__((always_inline)) {
     const int i0 = q0_cur;
     const bool f0 = flag_cur;
+    float b0 = bias_cur;
+    if (MOD == kModAdd) asm volatile("" : "+v"(b0));
     QVals nv{INFINITY, 0.0f, -1};
     if (it + 1 < n_iter) {
       const Step nx = next_step(st);
@@ -845,8 +861,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       flag_cur = tile_flag(nx.t);
       load_tiles(nx, q1, q_nxt, o_nxt);
       if (wave == 0) nv = fetch_qvals(nx, q1);
+      if (MOD == kModAdd) bias_cur = bias_coeff_uniform(a.score, nx.hq, a.Hq);
     }
-    if (it < n_iter) tile_step(st, i0, f0, q_cur, o_cur, l_cur, d_cur, c_cur);
+    if (it < n_iter) tile_step(i0, f0, b0 * kLog2e, q_cur, o_cur, l_cur, d_cur, c_cur);
     if (wave == 0 && it + 1 < n_iter) store_qvals(nv, l_nxt, d_nxt, c_nxt);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

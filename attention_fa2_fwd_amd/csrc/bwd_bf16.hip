@@ -761,12 +761,28 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // S = Q K^T and dP = dO V^T for the 32 queries: element r is query
     // i0 + 8 (r / 4) + 4h + r % 4, key kj.
     f32x16 s = f32x16{}, dp = f32x16{};
+    // Each chunk's Q, dO and V fragments are read LAS chunks ahead of their
+    // products, so the LDS latency is not waited out product by product (the
+    // D = 128 document variants with a bias have no registers for it).
+    constexpr int LAS = (D == 128 && DOC && MOD == kModAdd) ? 0 : 1;
+    struct SOps {
+      bf16x8 q, o, v;
+    };
+    auto rd_s = [&](int c) __attribute__((always_inline)) -> SOps {
+      const int o = ((c & 1) ? rd_row1 : rd_row0) + 32 * c;
+      return SOps{*(const bf16x8 *)(qt_ + o), *(const bf16x8 *)(ot + o), *(const bf16x8 *)(vrow + 32 * c)};
+    };
+    SOps sq[LAS + 1];
+#pragma unroll
+    for (int c = 0; c < LAS; ++c) sq[c] = rd_s(c);
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
-      const int o = ((c & 1) ? rd_row1 : rd_row0) + 32 * c;
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(qt_ + o), kf[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(ot + o),
-                                                   *(const bf16x8 *)(vrow + 32 * c), dp, 0, 0, 0);
+      if (c + LAS < NDC) sq[(c + LAS) % (LAS + 1)] = rd_s(c + LAS);
+      if (LAS > 0) __builtin_amdgcn_sched_barrier(0);
+      const SOps &x = sq[c % (LAS + 1)];
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x.q, kf[c], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x.o, x.v, dp, 0, 0, 0);
+      if (LAS > 0) __builtin_amdgcn_sched_barrier(0);
     }
     // P and dS go to bf16 as soon as they are formed (two 16-query chunks of
     // 8 values per lane each), which keeps the live set small.
@@ -804,27 +820,37 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       sw[2 * g] = pack_bf16x2(dr[0], dr[1]);
       sw[2 * g + 1] = pack_bf16x2(dr[2], dr[3]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time.
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time: the products
+    // in order (c, db, dV then dK), each transposed operand read LA products
+    // ahead of its use.
     const char *obase0 = ot + rd_tr0, *obase1 = ot + rd_tr1;
     const char *qbase0 = qt_ + rd_tr0, *qbase1 = qt_ + rd_tr1;
+    constexpr int NM = 4 * NDB, LA = 2;
+    auto rd_op = [&](int m) __attribute__((always_inline)) -> u32x4 {
+      const int c = m / (2 * NDB), db = (m >> 1) % NDB;
+      const char *b0 = (m & 1) ? qbase0 : obase0, *b1 = (m & 1) ? qbase1 : obase1;
+      const s16x4 lo = lds_read_tr(b0 + T::tr_step(c, 0) + 64 * db);
+      const s16x4 hi = lds_read_tr(b1 + T::tr_step(c, 1) + 64 * db);
+      return u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                   __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+    };
+    u32x4 opq[LA + 1];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]});
-      const bf16x8 sb = __builtin_bit_cast(bf16x8, u32x4{sw[4 * c], sw[4 * c + 1], sw[4 * c + 2], sw[4 * c + 3]});
-      asm volatile("" ::: "memory");   // keep this chunk's LDS reads in the chunk
+    for (int m = 0; m < LA; ++m) opq[m] = rd_op(m);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const s16x4 olo = lds_read_tr(obase0 + T::tr_step(c, 0) + 64 * db);
-        const s16x4 ohi = lds_read_tr(obase1 + T::tr_step(c, 1) + 64 * db);
-        const u32x4 ow = {__builtin_bit_cast(u32x2, olo)[0], __builtin_bit_cast(u32x2, olo)[1],
-                          __builtin_bit_cast(u32x2, ohi)[0], __builtin_bit_cast(u32x2, ohi)[1]};
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ow), pb, dv[db], 0, 0, 0);
-        const s16x4 qlo = lds_read_tr(qbase0 + T::tr_step(c, 0) + 64 * db);
-        const s16x4 qhi = lds_read_tr(qbase1 + T::tr_step(c, 1) + 64 * db);
-        const u32x4 qw = {__builtin_bit_cast(u32x2, qlo)[0], __builtin_bit_cast(u32x2, qlo)[1],
-                          __builtin_bit_cast(u32x2, qhi)[0], __builtin_bit_cast(u32x2, qhi)[1]};
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qw), sb, dk[db], 0, 0, 0);
+    for (int m = 0; m < NM; ++m) {
+      if (m + LA < NM) opq[(m + LA) % (LA + 1)] = rd_op(m + LA);
+      __builtin_amdgcn_sched_barrier(0);
+      const int c = m / (2 * NDB), db = (m >> 1) % NDB;
+      const bf16x8 op = __builtin_bit_cast(bf16x8, opq[m % (LA + 1)]);
+      if (m & 1) {
+        const bf16x8 sb = __builtin_bit_cast(bf16x8, u32x4{sw[4 * c], sw[4 * c + 1], sw[4 * c + 2], sw[4 * c + 3]});
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, sb, dk[db], 0, 0, 0);
+      } else {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]});
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pb, dv[db], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 

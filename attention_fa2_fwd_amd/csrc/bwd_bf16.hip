@@ -44,6 +44,12 @@
 // launch first in both passes (with a BlockMask, ranked by list length).
 #include "kernels.h"
 
+// Every fused multiply-add here is written as one: with implicit
+// contraction the compiler fused a product into a later sum in some
+// places and not in others, depending on how the surrounding code was
+// laid out, so equal formulas could round differently between builds.
+#pragma clang fp contract(off)
+
 namespace attn {
 namespace {
 
@@ -231,6 +237,11 @@ __device__ __forceinline__ float mod_score(float s, float c_log2, float bias2, f
   if (MOD == kModCap) return softcap_log2_fast(s, cap_k, cap2);
   if (MOD == kModRaw) return s * c_log2;
   return __builtin_fmaf(s, c_log2, __builtin_fmaf(bias2, off, base));
+}
+// log2 P = x - LSE (log2 units); for raw scores x = c s, taken as one FMA.
+template <int MOD>
+__device__ __forceinline__ float log2_p_arg(float s, float c_log2, float x, float lse2) {
+  return (MOD == kModRaw) ? __builtin_fmaf(s, c_log2, -lse2) : x - lse2;
 }
 template <int MOD>
 __device__ __forceinline__ float mod_grad(float x, float inv_cap2) {
@@ -445,16 +456,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
                       (k0 + kKTile <= a.Skv);
     // S^T and dP^T for the two 32-key blocks.
     f32x16 s[2], dp[2];
+    // The K and V fragments of chunk n = NDC kb + c are read LAQ chunks ahead
+    // of their products (the D = 128 soft-cap variants have no registers for
+    // it).
+    constexpr int LAQ = (D == 128 && MOD == kModCap) ? 0 : 1, NQ = 2 * NDC;
+    struct QOps {
+      bf16x8 k, v;
+    };
+    auto rd_q = [&](int n) __attribute__((always_inline)) -> QOps {
+      const int kb = n / NDC, c = n % NDC;
+      const int o = ((c & 1) ? rd_row1 : rd_row0) + T::row_step(kb) + 32 * c;
+      return QOps{*(const bf16x8 *)(kt + o), *(const bf16x8 *)(vt + o)};
+    };
+    QOps qq[LAQ + 1];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+    for (int n = 0; n < LAQ; ++n) qq[n] = rd_q(n);
 #pragma unroll
-      for (int c = 0; c < NDC; ++c) {
-        const int o = ((c & 1) ? rd_row1 : rd_row0) + T::row_step(kb) + 32 * c;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(kt + o), qf[c], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(vt + o), df[c], dp[kb], 0, 0, 0);
+    for (int n = 0; n < NQ; ++n) {
+      const int kb = n / NDC, c = n % NDC;
+      if (c == 0) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
       }
+      if (n + LAQ < NQ) qq[(n + LAQ) % (LAQ + 1)] = rd_q(n + LAQ);
+      if (LAQ > 0) __builtin_amdgcn_sched_barrier(0);
+      const QOps &x = qq[n % (LAQ + 1)];
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x.k, qf[c], s[kb], 0, 0, 0);
+      dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x.v, df[c], dp[kb], 0, 0, 0);
+      if (LAQ > 0) __builtin_amdgcn_sched_barrier(0);
     }
     // dS^T element r of block kb: key j = k0 + 32 kb + 8 (r / 4) + 4h + r % 4.
     const int jb = k0 + 4 * h;
@@ -466,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
         const int j = jb + off;
         const float x = mod_score<MOD>(s[kb][r], c_log2, bias2, cap_k, cap2, bias_base, (float)off);
-        float p = fast_exp2(x - lse2);
+        float p = fast_exp2(log2_p_arg<MOD>(s[kb][r], c_log2, x, lse2));
         if (!full) {
           const int doc_j = DOC ? kdoc[4 * h + off] : 0;
           const bool vis = (j < a.Skv) && pair_visible<MASK>(a.mask, qi, j, doc_i, doc_j);
@@ -761,10 +790,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // S = Q K^T and dP = dO V^T for the 32 queries: element r is query
     // i0 + 8 (r / 4) + 4h + r % 4, key kj.
     f32x16 s = f32x16{}, dp = f32x16{};
-    // Each chunk's Q, dO and V fragments are read LAS chunks ahead of their
-    // products, so the LDS latency is not waited out product by product (the
-    // D = 128 document variants with a bias have no registers for it).
-    constexpr int LAS = (D == 128 && DOC && MOD == kModAdd) ? 0 : 1;
+    // Each chunk's Q, dO and V fragments are read LAS chunks ahead.
+    constexpr int LAS = (D == 128 && DOC && MOD == kModAdd) ? 0 : 1;   // (0: the D = 128 document variants with a bias would spill)
     struct SOps {
       bf16x8 q, o, v;
     };
@@ -805,7 +832,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
         const int r = 4 * g + e;
         const int i = i0 + qo + e;
         const float x = mod_score<MOD>(s[r], c_log2, bias2, cap_k, cap2, bias_base, (float)(-(8 * g + e)));
-        float pe = fast_exp2(x - l4[e]);
+        float pe = fast_exp2(log2_p_arg<MOD>(s[r], c_log2, x, l4[e]));
         if (DOC) {
           const int doc_i = (e == 0) ? c4.x : (e == 1) ? c4.y : (e == 2) ? c4.z : c4.w;
           pe = (full || pair_visible<MASK>(a.mask, i, kj, doc_i, doc_j)) ? pe : 0.0f;
@@ -825,7 +852,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // ahead of its use.
     const char *obase0 = ot + rd_tr0, *obase1 = ot + rd_tr1;
     const char *qbase0 = qt_ + rd_tr0, *qbase1 = qt_ + rd_tr1;
-    constexpr int NM = 4 * NDB, LA = 2;
+    constexpr int NM = 4 * NDB, LA = (D == 64) ? 2 : 2;
     auto rd_op = [&](int m) __attribute__((always_inline)) -> u32x4 {
       const int c = m / (2 * NDB), db = (m >> 1) % NDB;
       const char *b0 = (m & 1) ? qbase0 : obase0, *b1 = (m & 1) ? qbase1 : obase1;

@@ -230,7 +230,8 @@ __device__ __forceinline__ float bias_coeff_uniform(const ScoreArgs &s, int hq, 
 // Log2-domain modified score of raw dot product s, and the factor
 // score_mod'(x) of the chain rule.  With a bias, bias2 (j - i) is passed as
 // base + bias2 * off: base per tile and lane, off a compile-time offset of
-// the accumulator element, so the bias costs one FMA.
+// the accumulator element, so the bias costs one FMA.  (Where only log2 P is
+// needed, the kernels fold the LSE into base instead.)
 template <int MOD>
 __device__ __forceinline__ float mod_score(float s, float c_log2, float bias2, float cap_k, float cap2,
                                            float base, float off) {
@@ -488,6 +489,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     // dS^T element r of block kb: key j = k0 + 32 kb + 8 (r / 4) + 4h + r % 4.
     const int jb = k0 + 4 * h;
     const float bias_base = bias2 * (float)(jb - qi);   // j - i = (jb - qi) + off
+    // With a bias, log2 P = c s + bias2 off + (bias_base - LSE): the row's
+    // LSE goes into the tile's base, two FMAs per score.
+    const float base_lse = bias_base - lse2;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -495,7 +499,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
         const int j = jb + off;
         const float x = mod_score<MOD>(s[kb][r], c_log2, bias2, cap_k, cap2, bias_base, (float)off);
-        float p = fast_exp2(log2_p_arg<MOD>(s[kb][r], c_log2, x, lse2));
+        float p = fast_exp2((MOD == kModAdd) ? mod_score<MOD>(s[kb][r], c_log2, bias2, cap_k, cap2, base_lse, (float)off)
+                                             : log2_p_arg<MOD>(s[kb][r], c_log2, x, lse2));
         if (!full) {
           const int doc_j = DOC ? kdoc[4 * h + off] : 0;
           const bool vis = (j < a.Skv) && pair_visible<MASK>(a.mask, qi, j, doc_i, doc_j);
@@ -768,11 +773,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
     return r;
   };
-  auto store_qvals = [&](const QVals &r, float *ls, float *dt, int32_t *dc) __attribute__((always_inline)) {
+  // With a bias the staged value also carries the query part of the bias,
+  // bias2 (i - j0) for query i = q0s + lane (bias2 the step's coefficient in
+  // log2 units); j0 keeps both parts small where pairs are near.
+  auto store_qvals = [&](const QVals &r, float *ls, float *dt, int32_t *dc, int q0s, float bias2s)
+      __attribute__((always_inline)) {
     if (lane < kQTile) {
       float lse = r.lse;
       asm volatile("" : "+v"(lse));
-      ls[lane] = lse * kLog2e;
+      const float lse2 = lse * kLog2e;
+      ls[lane] = (MOD == kModAdd) ? __builtin_fmaf(bias2s, (float)(q0s + lane - j0), lse2) : lse2;
       dt[lane] = r.dot;
       if (DOC) dc[lane] = r.doc;
     }
@@ -814,8 +824,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // P and dS go to bf16 as soon as they are formed (two 16-query chunks of
     // 8 values per lane each), which keeps the live set small.
     uint32_t pw[8], sw[8];
-    // j - i = (kj - i0 - 4h) - (8g + e) for element 4g + e
-    const float bias_base = bias2 * (float)(kj - i0 - 4 * h);
+    // With a bias, the query part of bias2 (j - i) = bias2 (kj - j0) -
+    // bias2 (i - j0) is folded into the staged per-query value (see
+    // store_qvals), so log2 P = c s + (bias2 (kj - j0) - staged): two ops.
+    const float bias_key = (MOD == kModAdd) ? bias2 * (float)(kj - j0) : 0.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qo = 8 * g + 4 * h;   // query offset of elements 4g .. 4g + 3
@@ -831,8 +843,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
         const int i = i0 + qo + e;
-        const float x = mod_score<MOD>(s[r], c_log2, bias2, cap_k, cap2, bias_base, (float)(-(8 * g + e)));
-        float pe = fast_exp2(log2_p_arg<MOD>(s[r], c_log2, x, l4[e]));
+        const float x = mod_score<MOD>(s[r], c_log2, bias2, cap_k, cap2, 0.0f, 0.0f);
+        float pe = fast_exp2((MOD == kModAdd) ? __builtin_fmaf(s[r], c_log2, bias_key - l4[e])
+                                              : log2_p_arg<MOD>(s[r], c_log2, x, l4[e]));
         if (DOC) {
           const int doc_i = (e == 0) ? c4.x : (e == 1) ? c4.y : (e == 2) ? c4.z : c4.w;
           pe = (full || pair_visible<MASK>(a.mask, i, kj, doc_i, doc_j)) ? pe : 0.0f;
@@ -882,9 +895,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   const Step first{hkv * G, 0};
+  // The bias coefficient of the step's query head is carried from the
+  // iteration before, as the step's first query and full flag are below:
+  // taken where it is needed, its optional table load made the wave wait
+  // there for the next tiles' loads as well.  The empty asm keeps the log2
+  // scaling at the use.
+  float bias_cur = (MOD == kModAdd) ? bias_coeff_uniform(a.score, first.hq, a.Hq) : 0.0f;
   if (n_iter > 0) {
-    load_tiles(first, tile_q0(first.t), q_lds0, o_lds0);
-    if (wave == 0) store_qvals(fetch_qvals(first, tile_q0(first.t)), qv_lse0, qv_dot0, qv_doc0);
+    const int q0f = __builtin_amdgcn_readfirstlane(tile_q0(first.t));
+    load_tiles(first, q0f, q_lds0, o_lds0);
+    if (wave == 0) store_qvals(fetch_qvals(first, q0f), qv_lse0, qv_dot0, qv_doc0, q0f, bias_cur * kLog2e);
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
@@ -892,11 +912,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // iteration that loaded it, so an iteration looks up one list entry.
   int q0_cur = (n_iter > 0) ? __builtin_amdgcn_readfirstlane(tile_q0(first.t)) : 0;
   bool flag_cur = (n_iter > 0) && tile_flag(first.t);
-  // The bias coefficient of the step's query head is carried the same way:
-  // taken where it is needed, its optional table load made the wave wait
-  // there for the next tiles' loads as well.  The empty asm keeps the log2
-  // scaling at the use.
-  float bias_cur = (MOD == kModAdd) ? bias_coeff_uniform(a.score, first.hq, a.Hq) : 0.0f;
   // Iteration it (step st): load step it + 1 into the buffers step it - 1
   // used, compute step it, wait for this wave's loads, barrier.
   auto iteration = [&](int it, Step st, char *q_cur, char *o_cur, float *l_cur, float *d_cur,
@@ -917,7 +932,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       if (MOD == kModAdd) bias_cur = bias_coeff_uniform(a.score, nx.hq, a.Hq);
     }
     if (it < n_iter) tile_step(i0, f0, b0 * kLog2e, q_cur, o_cur, l_cur, d_cur, c_cur);
-    if (wave == 0 && it + 1 < n_iter) store_qvals(nv, l_nxt, d_nxt, c_nxt);
+    if (wave == 0 && it + 1 < n_iter) store_qvals(nv, l_nxt, d_nxt, c_nxt, q0_cur, bias_cur * kLog2e);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };

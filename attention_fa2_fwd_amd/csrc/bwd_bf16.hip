@@ -453,8 +453,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     const bool pos_full = (MASK == ATTN_MASK_DOCUMENT) ? (k0 + kKTile - 1 <= qw0)
                         : (MASK == kMaskDocWindow) ? ((k0 + kKTile - 1 <= qw0) && (qw1 - k0 < a.mask.window))
                         : false;
-    const bool full = (flag || block_full<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1) || (one_id && pos_full)) &&
-                      (k0 + kKTile <= a.Skv);
+    // Wave-uniform by construction; readfirstlane tells the compiler so, and
+    // the test below becomes one branch per tile instead of an exec-mask
+    // branch around every score.
+    const bool full = __builtin_amdgcn_readfirstlane(
+        (flag || block_full<MASK>(a.mask, qw0, qw1, k0, k0 + kKTile - 1) || (one_id && pos_full)) &&
+        (k0 + kKTile <= a.Skv));
     // S^T and dP^T for the two 32-key blocks.
     f32x16 s[2], dp[2];
     // The K and V fragments of chunk n = NDC kb + c are read LAQ chunks ahead
@@ -492,6 +496,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     // With a bias, log2 P = c s + bias2 off + (bias_base - LSE): the row's
     // LSE goes into the tile's base, two FMAs per score.
     const float base_lse = bias_base - lse2;
+    int4 kd4 = int4{0, 0, 0, 0};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -502,7 +507,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         float p = fast_exp2((MOD == kModAdd) ? mod_score<MOD>(s[kb][r], c_log2, bias2, cap_k, cap2, base_lse, (float)off)
                                              : log2_p_arg<MOD>(s[kb][r], c_log2, x, lse2));
         if (!full) {
-          const int doc_j = DOC ? kdoc[4 * h + off] : 0;
+          // The keys' document ids, four at a time (keys off .. off + 3 of
+          // the group are consecutive): one LDS read per four scores.
+          if (DOC && (r & 3) == 0) kd4 = *(const int4 *)(kdoc + 4 * h + off);
+          const int doc_j = !DOC ? 0 : (r & 3) == 0 ? kd4.x : (r & 3) == 1 ? kd4.y : (r & 3) == 2 ? kd4.z : kd4.w;
           const bool vis = (j < a.Skv) && pair_visible<MASK>(a.mask, qi, j, doc_i, doc_j);
           p = vis ? p : 0.0f;
         }

@@ -219,6 +219,33 @@ def test_bwd_causal_headline_shape_whole_heads():
         compare_grads((dq[sl], dk[sl], dv[sl]), ref, f"bwd causal headline b{b} h{hq}")
 
 
+def test_bwd_gqa_window_alibi_headline_shape_one_kv_group():
+    """The GQA window 1024 + ALiBi backward at its benchmarked shape (B=2,
+    Hq=32, Hkv=8, S=8192, D=128): one whole kv group (the last batch row's kv
+    head 7 and its query heads 28..31) against the oracle, dQ of the four
+    heads and the group's dK, dV.  Far positions make the bias terms large,
+    which the kernels split into a per-query and a per-key part."""
+    w = workloads.GQA_WINDOW_ALIBI
+    dev = torch.device("cuda")
+    q, k, v = workloads.randn_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, "bf16", w.seed)
+    do = workloads.randn_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, "bf16", w.seed + 1000)[0]
+    kw = dict(mask="sliding", window=w.window, score="alibi")
+    announce("bwd gqa window alibi headline shape, kv group b1 h7")
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    out, lse = af.attn_fwd(qd, kd, vd, **kw)
+    dq, dk, dv = af.attn_bwd(qd, kd, vd, out, lse, dod, **kw)
+    torch.cuda.synchronize()
+    b, hkv, g = w.B - 1, w.Hkv - 1, w.Hq // w.Hkv
+    hs = slice(hkv * g, hkv * g + g)
+    slopes = oracle.alibi_slopes(w.Hq)[hs]
+    ref = oracle.attention_backward_ref(f64(q[b:b + 1, hs]), f64(k[b:b + 1, hkv:hkv + 1]),
+                                        f64(v[b:b + 1, hkv:hkv + 1]), f64(do[b:b + 1, hs]),
+                                        1.0 / math.sqrt(w.D), oracle.MaskSpec(oracle.MASK_SLIDING, window=w.window),
+                                        oracle.ScoreSpec(oracle.SCORE_ALIBI, slopes=slopes))
+    compare_grads((dq[b:b + 1, hs], dk[b:b + 1, hkv:hkv + 1], dv[b:b + 1, hkv:hkv + 1]), ref,
+                  "bwd gqa window alibi headline shape")
+
+
 @pytest.mark.parametrize("mask", ["document", "sliding&document"])
 def test_bwd_block_mask_work_order_per_batch_rows(mask):
     """Both backward passes take BlockMask tiles in order of listed work,

@@ -246,6 +246,43 @@ def test_bwd_gqa_window_alibi_headline_shape_one_kv_group():
                   "bwd gqa window alibi headline shape")
 
 
+def test_bwd_document_block_mask_headline_shape_sampled_dq_rows():
+    """The document BlockMask backward at its benchmarked shape (B=1, H=16,
+    S=16384, D=128, the drawn document layout): dQ on sampled rows of two
+    heads (the first and last row of the first documents, and rows spread
+    over the sequence) against the oracle's rows, which need only those
+    rows' scores."""
+    w = workloads.DOCUMENT_BLOCKMASK
+    dev = torch.device("cuda")
+    inp = workloads.prefill_inputs(w)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    ids = inp["doc_ids"]
+    do = workloads.randn_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, "bf16", w.seed + 1000)[0]
+    qd, kd, vd, dod, dd = q.to(dev), k.to(dev), v.to(dev), do.to(dev), ids.to(dev)
+    announce("bwd document BlockMask headline shape, sampled dq rows")
+    out, lse = af.attn_fwd(qd, kd, vd, mask="document", doc_ids=dd)
+    bm = af.attn_block_mask_transpose(af.attn_build_block_mask("document", w.B, w.Sq, w.Skv, doc_ids=dd,
+                                                               device=dev))
+    dq, _, _ = af.attn_bwd(qd, kd, vd, out, lse, dod, mask="document", doc_ids=dd, block_mask=bm)
+    torch.cuda.synchronize()
+    starts = np.cumsum([0] + list(inp["doc_lengths"]))
+    rows = set(np.linspace(0, w.Sq - 1, 24).astype(int).tolist())
+    for a_, b_ in zip(starts[:12], starts[1:13]):
+        rows.update((int(a_), int(b_) - 1))
+    rows = np.array(sorted(r for r in rows if r < w.Sq))
+    ms = oracle.MaskSpec(oracle.MASK_DOCUMENT, doc_ids=ids.numpy())
+    for hq in (0, w.Hq - 1):
+        dq_ref, _, _ = oracle.attention_backward_rows(f64(q[0, hq])[rows], f64(k[0, hq]), f64(v[0, hq]),
+                                                      f64(do[0, hq])[rows], rows, 0, hq, w.Hq,
+                                                      1.0 / math.sqrt(w.D), ms)
+        got = f64(dq[0, hq])[rows]
+        err = np.abs(got - dq_ref)
+        a = err.max() / max(np.abs(dq_ref).max(), FLOOR)
+        m = err.mean() / max(np.abs(dq_ref).mean(), FLOOR)
+        print(f"bwd document headline h{hq} {len(rows)} rows: dq max/|max| {a:.2e} mean/|mean| {m:.2e}", flush=True)
+        assert a <= BWD_MAX_REL and m <= BWD_MEAN_REL, (hq, a, m)
+
+
 @pytest.mark.parametrize("mask", ["document", "sliding&document"])
 def test_bwd_block_mask_work_order_per_batch_rows(mask):
     """Both backward passes take BlockMask tiles in order of listed work,

@@ -16,9 +16,11 @@
 //   dV  = P^T dO,  dK = s dX^T Q                 (bwd_dkdv_kernel, after it)
 //
 // The two main kernels reuse the forward kernel's MFMA conventions
-// (v_mfma_f32_32x32x16_bf16, 4 waves x 32 rows, LDS tiles of 1 KiB row
-// blocks filled by buffer_load ... lds and read either row-wise or through
-// the transposing ds_read_b64_tr_b16):
+// (v_mfma_f32_32x32x16_bf16, 4 waves x 32 rows, LDS tiles of 1 KiB blocks
+// filled by buffer_load ... lds), but read each streamed tile both row-wise
+// and through the transposing ds_read_b64_tr_b16, so their tiles place rows
+// and permute chunks to keep both kinds of read free of bank conflicts
+// (Tile below):
 //  * bwd_dq_kernel, one workgroup per (b, hq, 128 query rows) (with groups
 //    of four or more query heads and no BlockMask, per 32 positions of four
 //    heads sharing a kv head, one head per wave), streams 64-key tiles of K
@@ -31,7 +33,7 @@
 //  * bwd_dkdv_kernel, one workgroup per (b, hkv, 128 keys), streams 32-row
 //    tiles of Q and dO for every query head of the GQA group, so dK and dV
 //    sum the group in registers.  S = Q K^T and dP = dO V^T take Q and dO
-//    rows from LDS and K, V (kept in registers) as the B operand; the lane
+//    rows from LDS, K from registers and V from a per-wave LDS copy; the lane
 //    then holds one key, P and dS are already the B operands of
 //    dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed
 //    from the same LDS tiles.  Per-query LSE and D are staged in LDS with the

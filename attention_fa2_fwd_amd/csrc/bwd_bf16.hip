@@ -810,8 +810,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // S = Q K^T and dP = dO V^T for the 32 queries: element r is query
     // i0 + 8 (r / 4) + 4h + r % 4, key kj.
     f32x16 s = f32x16{}, dp = f32x16{};
-    // Each chunk's Q, dO and V fragments are read LAS chunks ahead.
-    constexpr int LAS = (D == 128 && DOC && MOD == kModAdd) ? 0 : 1;   // (0: the D = 128 document variants with a bias would spill)
+    // Each chunk's Q, dO and V fragments are read LAS chunks ahead of their
+    // products, so the LDS latency is not waited out product by product (the
+    // D = 128 document variants with a bias have no registers for it).
+    constexpr int LAS = (D == 128 && DOC && MOD == kModAdd) ? 0 : 1;
     struct SOps {
       bf16x8 q, o, v;
     };
@@ -875,7 +877,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // ahead of its use.
     const char *obase0 = ot + rd_tr0, *obase1 = ot + rd_tr1;
     const char *qbase0 = qt_ + rd_tr0, *qbase1 = qt_ + rd_tr1;
-    constexpr int NM = 4 * NDB, LA = (D == 64) ? 2 : 2;
+    constexpr int NM = 4 * NDB, LA = 2;
     auto rd_op = [&](int m) __attribute__((always_inline)) -> u32x4 {
       const int c = m / (2 * NDB), db = (m >> 1) % NDB;
       const char *b0 = (m & 1) ? qbase0 : obase0, *b1 = (m & 1) ? qbase1 : obase1;

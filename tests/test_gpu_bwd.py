@@ -219,6 +219,16 @@ def test_bwd_causal_headline_shape_whole_heads():
         compare_grads((dq[sl], dk[sl], dv[sl]), ref, f"bwd causal headline b{b} h{hq}")
 
 
+@pytest.mark.parametrize("mask", ["causal", "none"])
+def test_bwd_alibi_long_rows(mask):
+    """ALiBi backward over 4096 positions without a window (B=1, Hq=4, Hkv=1,
+    D=64): the kernels split bias2 (j - i) into a per-query and a per-key
+    part relative to the workgroup's first key, whose magnitudes grow with
+    the distance; with no causal mask the later keys carry the largest
+    scores of each row."""
+    run_bwd(1, 4, 1, 4096, 4096, 64, mask, "alibi", seed=31)
+
+
 def test_bwd_gqa_window_alibi_headline_shape_one_kv_group():
     """The GQA window 1024 + ALiBi backward at its benchmarked shape (B=2,
     Hq=32, Hkv=8, S=8192, D=128): one whole kv group (the last batch row's kv

@@ -518,10 +518,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         }
         s[kb][r] = p * (dp[kb][r] - dsum) * mod_grad<MOD>(x, inv_cap2);
       }
-    // dQ^T += K^T dS^T, 16 keys at a time, at raised wave priority: the
-    // wave feeding the matrix cores issues ahead of the other wave's
-    // elementwise work (measured 6-9% faster on the causal D=64 backward).
-    __builtin_amdgcn_s_setprio(1);
+    // dQ^T += K^T dS^T, 16 keys at a time, at D = 64 at raised wave
+    // priority: the wave feeding the matrix cores issues ahead of the other
+    // wave's elementwise work (measured 6-9% faster on the causal D=64
+    // backward; at D = 128 the GQA window backward ran 2.6-2.8% faster
+    // without it).
+    if (D == 64) __builtin_amdgcn_s_setprio(1);
     const char *kbase0 = kt + rd_tr0, *kbase1 = kt + rd_tr1;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kw), pb, acc[db], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
+    if (D == 64) __builtin_amdgcn_s_setprio(0);
   };
 
   // Double-buffered tile loop: iteration n loads tile n + 1 into the buffers
